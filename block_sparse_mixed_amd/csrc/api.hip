@@ -1,0 +1,68 @@
+// C-ABI entry points that enqueue work: argument checks, then kernel launches.
+// Every check happens before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "da2_internal.hpp"
+
+namespace da2 {
+hipError_t launch_prep(const Geo& g, const Layout& L, const void* q, const void* k, const void* v, void* ws,
+                       hipStream_t stream);
+hipError_t launch_draft(const Geo& g, const Layout& L, void* ws, hipStream_t stream);
+hipError_t launch_set_labels(const Geo& g, const Layout& L, void* ws, const int8_t* labels, hipStream_t stream);
+hipError_t launch_attention(const Geo& g, const Layout& L, const void* ws, void* out, int out_fp32,
+                            hipStream_t stream);
+}  // namespace da2
+
+namespace {
+
+da2_status check_ws(const da2_plan_t* plan, const void* ws, size_t bytes) {
+    if (!ws) return DA2_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return DA2_ERR_WORKSPACE;
+    if (bytes < plan->ws.total) return DA2_ERR_WORKSPACE;
+    return DA2_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// 16-byte vector loads/stores of rows need 8-element alignment of the strides.
+bool strides_vectorizable(const da2::Geo& g) {
+    return g.stride_n % 8 == 0 && g.stride_h % 8 == 0 && g.stride_b % 8 == 0;
+}
+
+}  // namespace
+
+extern "C" da2_status da2_prepare(const da2_plan_t* plan, const void* q, const void* k, const void* v,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream) {
+    if (!plan || !q || !k || !v) return DA2_ERR_INVALID_ARG;
+    da2_status st = check_ws(plan, workspace, workspace_bytes);
+    if (st != DA2_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !strides_vectorizable(plan->geo)) return DA2_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (da2::launch_prep(plan->geo, plan->ws, q, k, v, workspace, s) != hipSuccess) return DA2_ERR_HIP;
+    if (da2::launch_draft(plan->geo, plan->ws, workspace, s) != hipSuccess) return DA2_ERR_HIP;
+    return DA2_OK;
+}
+
+extern "C" da2_status da2_attention(const da2_plan_t* plan, const void* workspace, size_t workspace_bytes, void* out,
+                                    void* hip_stream) {
+    if (!plan || !out) return DA2_ERR_INVALID_ARG;
+    da2_status st = check_ws(plan, workspace, workspace_bytes);
+    if (st != DA2_OK) return st;
+    if (!aligned16(out) || !strides_vectorizable(plan->geo)) return DA2_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (da2::launch_attention(plan->geo, plan->ws, workspace, out, plan->cfg.out_dtype == DA2_OUT_FP32, s) != hipSuccess)
+        return DA2_ERR_HIP;
+    return DA2_OK;
+}
+
+extern "C" da2_status da2_set_labels(const da2_plan_t* plan, void* workspace, size_t workspace_bytes,
+                                     const int8_t* labels_dev, void* hip_stream) {
+    if (!plan || !labels_dev) return DA2_ERR_INVALID_ARG;
+    da2_status st = check_ws(plan, workspace, workspace_bytes);
+    if (st != DA2_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (da2::launch_set_labels(plan->geo, plan->ws, workspace, labels_dev, s) != hipSuccess) return DA2_ERR_HIP;
+    return DA2_OK;
+}

@@ -1,0 +1,31 @@
+// Internal declarations shared by the host plan code and the kernel launchers.
+#pragma once
+
+#include <cstdint>
+
+#include "da2.h"
+
+namespace da2 {
+
+// Geometry and sizes every kernel needs, passed by value.
+struct Geo {
+    int32_t frames, grid_h, grid_w, win_h, win_w;
+    int32_t n_wy, n_wx, n_blocks, block_size, head_dim, heads, bh;
+    int32_t n_hi, n_lo;
+    int64_t tokens;
+    int64_t stride_b, stride_h, stride_n;
+    double tau;
+};
+
+struct Layout {
+    uint64_t pool, q8, k8, qb, kb, v8t, e8, q4, k4, v4t, sq4, sk4, sv4t, scores, labels, hi, lo, status;
+    uint64_t total;
+};
+
+}  // namespace da2
+
+struct da2_plan_s {
+    da2_config cfg;
+    da2::Geo geo;
+    da2::Layout ws;
+};

@@ -1,0 +1,176 @@
+/*
+ * da2.h - C ABI of the DraftAttention2 hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The path replaces one attention call of a video diffusion transformer over
+ * spatiotemporal latent tokens [DraftAttention2 (arXiv 2609.32628), abstract;
+ * DraftAttention (arXiv 2505.14708), abstract]:
+ *
+ *   da2_plan       host only: validate a configuration, derive the window
+ *                  geometry, the per-row block budgets and the workspace layout.
+ *   da2_prepare    enqueue the fused operand preparation (pool + reorder +
+ *                  fp8/MXFP4 quantize) and the draft map + shared ranking.
+ *   da2_attention  enqueue the single block-sparse attention kernel with an
+ *                  fp8 phase and an MXFP4 phase that share the online-softmax
+ *                  state and the output accumulator; it writes outputs back in
+ *                  the original (raster) token order.
+ *
+ * Conventions
+ *  - Every device buffer (q, k, v, out, workspace, labels) is allocated and
+ *    owned by the caller. The library allocates no device memory and keeps no
+ *    global mutable state; a plan is an immutable host object, so calls on
+ *    different plans (or the same plan from different threads) are safe.
+ *  - Tensors q, k, v, out are [batch, heads, tokens, head_dim] addressed by
+ *    element strides (stride_b, stride_h, stride_n), head_dim contiguous.
+ *    Tokens are in raster order (frame, row, column) of a frames x grid_h x
+ *    grid_w latent grid. q, k, v are bf16; out is bf16 or fp32.
+ *  - Argument errors are reported synchronously, before anything is enqueued.
+ *    Kernel faults surface at the caller's next synchronisation, as usual in
+ *    HIP. No C++ exception crosses this interface.
+ *  - The workspace written by da2_prepare stays valid for da2_attention on
+ *    the same stream until it is overwritten; q, k, v may be released once
+ *    da2_prepare has completed on the stream.
+ */
+#ifndef DA2_H
+#define DA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum da2_status {
+    DA2_OK = 0,
+    DA2_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad budget, ... */
+    DA2_ERR_UNSUPPORTED = 2,   /* valid but outside what the kernels implement */
+    DA2_ERR_WORKSPACE = 3,     /* workspace too small or not 256-byte aligned */
+    DA2_ERR_HIP = 4            /* a HIP runtime call or launch failed */
+} da2_status;
+
+enum { DA2_OUT_BF16 = 0, DA2_OUT_FP32 = 1 };
+
+/* Block labels, one int8 per (query block, key block). */
+enum { DA2_SKIP = 0, DA2_LO = 1, DA2_HI = 2 };
+
+/* Tile geometry of the workspace: every block is stored as DA2_TILE slots of
+ * DA2_DPAD channels; slots beyond the window and channels beyond head_dim are
+ * zero. */
+#define DA2_TILE 128
+#define DA2_DPAD 128
+#define DA2_MAX_BLOCKS 4096
+
+typedef struct da2_config {
+    int32_t batch;
+    int32_t heads;
+    int32_t frames;
+    int32_t grid_h;           /* latent rows per frame */
+    int32_t grid_w;           /* latent columns per frame */
+    int32_t head_dim;         /* 32, 64, 96 or 128 */
+    int32_t win_h;            /* pooling window = one block: win_h x win_w tokens */
+    int32_t win_w;            /* win_h * win_w <= 128 */
+    double budget_hi;         /* fraction of key blocks per query block in fp8 */
+    double budget_lo;         /* fraction in MXFP4 (clamped to 1 - budget_hi) */
+    double softmax_scale;     /* tau; 0 selects 1/sqrt(head_dim) */
+    int64_t stride_b;         /* element strides shared by q, k, v and out; */
+    int64_t stride_h;         /* all three 0 selects the contiguous layout  */
+    int64_t stride_n;
+    int32_t out_dtype;        /* DA2_OUT_BF16 or DA2_OUT_FP32 */
+    uint32_t flags;           /* reserved, must be 0 */
+} da2_config;
+
+typedef struct da2_plan_s da2_plan_t;
+
+/* Workspace sections (byte offsets from the workspace base, each 256-byte
+ * aligned). BH = batch * heads, NB = n_blocks, T = DA2_TILE, P = DA2_DPAD.
+ *   pool    f64 [4][BH][NB][P]  mean Q, max Q, mean K, max K over the window's tokens
+ *   q8, k8  u8  [BH][NB][T][P]  E4M3 codes, slot-major
+ *   qb, kb  bf16 [BH][NB][T][P] the same E4M3 codes decoded to bf16 (exact, without
+ *                               the block scale): operands of the fp8 phase's QK^T
+ *   v8t     u8  [BH][NB][P][T]  E4M3 codes of V, channel-major (transposed tile)
+ *   e8      u8  [3][BH][NB]     E8M0 scale of each block for q, k, v
+ *   q4, k4  u8  [BH][NB][T][P/2] E2M1 codes, two per byte, low nibble = even channel
+ *   sq4,sk4 u8  [BH][NB][T][P/32] E8M0 scale per token per 32 channels
+ *   v4t     u8  [BH][NB][P][T/2] E2M1 codes of V, channel-major, low nibble = even slot
+ *   sv4t    u8  [BH][NB][P][T/32] E8M0 scale per channel per 32 slots
+ *   scores  f64 [2][BH][NB][NB] draft logits; after da2_prepare section 0 holds
+ *                               the combined block score C
+ *   labels  i8  [BH][NB][NB]   DA2_SKIP / DA2_LO / DA2_HI
+ *   hi, lo  i32 [BH][NB][n_hi], [BH][NB][n_lo]  ascending key-block indices
+ *   status  u32 [4]             [0]: rows whose labels had the wrong counts
+ *                               (written by da2_set_labels)
+ */
+typedef struct da2_plan_info_s {
+    int32_t n_blocks;
+    int32_t block_size;
+    int32_t n_wy;
+    int32_t n_wx;
+    int32_t n_hi;
+    int32_t n_lo;
+    int64_t tokens;
+    int64_t slots;            /* n_blocks * block_size */
+    double tau;
+    uint64_t workspace_bytes;
+    uint64_t off_pool, off_q8, off_k8, off_v8t, off_e8;
+    uint64_t off_q4, off_k4, off_v4t, off_sq4, off_sk4, off_sv4t;
+    uint64_t off_scores, off_labels, off_hi, off_lo, off_status;
+    uint64_t off_qb, off_kb;
+} da2_plan_info_t;
+
+/* Validate cfg and build a plan. Host only: touches no GPU state.
+ * Geometry [DraftAttention (arXiv 2505.14708), abstract; news article on it,
+ * method steps 1 and 4]: each frame is cut into win_h x win_w windows, padded
+ * up to whole windows; a window is one block. Budget counts per query block
+ * [DraftAttention2, abstract, configurable budgets]:
+ *   n_hi = floor(budget_hi * NB + 1/2),
+ *   n_ret = floor((budget_hi + min(budget_lo, 1 - budget_hi)) * NB + 1/2),
+ *   n_lo = n_ret - n_hi; n_ret = 0 is DA2_ERR_INVALID_ARG.
+ * On success *out owns a heap object; release it with da2_plan_destroy. */
+da2_status da2_plan(const da2_config* cfg, da2_plan_t** out);
+
+/* Free a plan; NULL is accepted. */
+void da2_plan_destroy(da2_plan_t* plan);
+
+/* Sizes, budget counts and workspace offsets of a plan. */
+da2_status da2_plan_info(const da2_plan_t* plan, da2_plan_info_t* out);
+
+/* Enqueue operand preparation and the draft ranking on hip_stream (a
+ * hipStream_t; NULL = the null stream). Asynchronous.
+ * [DraftAttention2, abstract]: 2D average- and max-pooled Q and K give a
+ * low-resolution draft attention map that scores every (query block, key
+ * block) pair; one shared ranking per query block labels the top n_hi key
+ * blocks fp8, the next n_lo MXFP4 and skips the rest (ties: lower index);
+ * operands are prepared once, reordered window-major and quantized to both
+ * fp8 E4M3 (one power-of-two scale per block) and MXFP4 (E8M0 per 32
+ * elements along the contraction axis).
+ * q, k, v: device bf16, layout per cfg. workspace: device, >= workspace_bytes,
+ * 256-byte aligned. Writes only the workspace. */
+da2_status da2_prepare(const da2_plan_t* plan, const void* q, const void* k, const void* v,
+                       void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Enqueue the phased block-sparse attention on hip_stream. Asynchronous.
+ * [DraftAttention2, abstract]: one kernel runs an fp8 phase over the hi
+ * blocks and an MXFP4 phase over the lo blocks, sharing data movement, the
+ * softmax statistics and the output accumulator; skipped blocks cost nothing.
+ * [DraftAttention, abstract]: outputs return to the original token order.
+ * workspace: as left by da2_prepare (or da2_set_labels). out: device, layout
+ * per cfg, dtype per cfg.out_dtype; every real token's row is written and
+ * nothing else. */
+da2_status da2_attention(const da2_plan_t* plan, const void* workspace, size_t workspace_bytes,
+                         void* out, void* hip_stream);
+
+/* Test hook, not for production: replace the labels in the workspace with
+ * labels_dev (device int8 [BH][NB][NB]) and rebuild the hi/lo lists. A row
+ * whose label counts differ from (n_hi, n_lo) is counted in status[0] (the
+ * count is reset first) and its lists are left unspecified. Asynchronous. */
+da2_status da2_set_labels(const da2_plan_t* plan, void* workspace, size_t workspace_bytes,
+                          const int8_t* labels_dev, void* hip_stream);
+
+/* Static, never-NULL description of a status code. */
+const char* da2_status_string(da2_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DA2_H */

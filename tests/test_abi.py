@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: exports, plan validation, counts and layout."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import block_sparse_mixed_amd as da2
+from oracle.draft import budget_counts
+from oracle.geometry import Geometry
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "da2.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(da2_\w+)\s*\([^;{]*\)\s*;", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert set(names) == set(da2.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", da2.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (da2_\w+)$", out, flags=re.M))
+    missing = set(names) - exported
+    assert not missing, missing
+    lib = ctypes.CDLL(da2.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def _cfg(**kw):
+    base = dict(batch=1, heads=12, frames=21, grid_h=30, grid_w=52, head_dim=128, win_h=8, win_w=16,
+                budget_hi=0.15, budget_lo=0.35)
+    base.update(kw)
+    return da2.make_config(**base)
+
+
+def test_plan_wan_shape_matches_oracle_geometry_and_counts():
+    p = da2.da2_plan(_cfg())
+    i = p.info
+    g = Geometry(21, 30, 52, 8, 16)
+    assert (i.n_blocks, i.block_size, i.n_wy, i.n_wx) == (g.n_blocks, 128, g.n_wy, g.n_wx) == (336, 128, 4, 4)
+    assert (i.n_hi, i.n_lo) == budget_counts(336, 0.15, 0.35) == (50, 118)
+    assert i.tokens == 32760 and i.slots == 43008
+    assert i.tau == pytest.approx(1 / np.sqrt(128), rel=0, abs=0)
+
+
+def test_budget_counts_agree_with_oracle_on_many_configs():
+    rng = np.random.default_rng(0)
+    for _ in range(300):
+        frames, gh, gw = rng.integers(1, 9), rng.integers(1, 40), rng.integers(1, 70)
+        wh, ww = [(4, 4), (8, 16), (8, 8), (2, 16)][rng.integers(0, 4)]
+        hi = float(rng.choice([0.0, 0.05, 0.1, 0.15, 0.25, 1 / 3, 0.5, 1.0, rng.random()]))
+        lo = float(rng.choice([0.0, 0.2, 0.35, 0.4, 1.0, rng.random()]))
+        nb = Geometry(int(frames), int(gh), int(gw), wh, ww).n_blocks
+        try:
+            want = budget_counts(nb, hi, lo)
+        except ValueError:
+            with pytest.raises(da2.Da2Error) as e:
+                da2.da2_plan(_cfg(frames=int(frames), grid_h=int(gh), grid_w=int(gw), win_h=wh, win_w=ww,
+                                  budget_hi=hi, budget_lo=lo))
+            assert e.value.status == da2.DA2_ERR_INVALID_ARG
+            continue
+        p = da2.da2_plan(_cfg(frames=int(frames), grid_h=int(gh), grid_w=int(gw), win_h=wh, win_w=ww,
+                              budget_hi=hi, budget_lo=lo))
+        assert (p.info.n_blocks, p.info.n_hi, p.info.n_lo) == (nb, *want)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), da2.DA2_ERR_INVALID_ARG),
+    (dict(head_dim=100), da2.DA2_ERR_UNSUPPORTED),
+    (dict(head_dim=256), da2.DA2_ERR_UNSUPPORTED),
+    (dict(win_h=16, win_w=16), da2.DA2_ERR_UNSUPPORTED),
+    (dict(budget_hi=-0.1), da2.DA2_ERR_INVALID_ARG),
+    (dict(budget_hi=1.5), da2.DA2_ERR_INVALID_ARG),
+    (dict(budget_hi=0.0, budget_lo=0.0), da2.DA2_ERR_INVALID_ARG),
+    (dict(out_dtype=7), da2.DA2_ERR_INVALID_ARG),
+    (dict(flags=1), da2.DA2_ERR_INVALID_ARG),
+    (dict(frames=200, grid_h=64, grid_w=64), da2.DA2_ERR_UNSUPPORTED),
+])
+def test_plan_rejects(kw, status):
+    with pytest.raises(da2.Da2Error) as e:
+        da2.da2_plan(_cfg(**kw))
+    assert e.value.status == status
+
+
+def test_plan_clamps_lo_budget():
+    p = da2.da2_plan(_cfg(budget_hi=1.0, budget_lo=0.4))
+    assert (p.info.n_hi, p.info.n_lo) == (336, 0)
+    p = da2.da2_plan(_cfg(budget_hi=0.0, budget_lo=1.0))
+    assert (p.info.n_hi, p.info.n_lo) == (0, 336)
+
+
+def test_workspace_layout_is_aligned_and_disjoint():
+    p = da2.da2_plan(_cfg())
+    i = p.info
+    bh, nb, T, P = 12, 336, 128, 128
+    sizes = {"pool": 4 * bh * nb * P * 8, "q8": bh * nb * T * P, "k8": bh * nb * T * P,
+             "qb": bh * nb * T * P * 2, "kb": bh * nb * T * P * 2, "v8t": bh * nb * P * T,
+             "e8": 3 * bh * nb, "q4": bh * nb * T * P // 2, "k4": bh * nb * T * P // 2, "v4t": bh * nb * P * T // 2,
+             "sq4": bh * nb * T * 4, "sk4": bh * nb * T * 4, "sv4t": bh * nb * P * 4, "scores": 2 * bh * nb * nb * 8,
+             "labels": bh * nb * nb, "hi": bh * nb * 50 * 4, "lo": bh * nb * 118 * 4, "status": 16}
+    spans = sorted((getattr(i, "off_" + k), getattr(i, "off_" + k) + v) for k, v in sizes.items())
+    for (a0, a1), (b0, _) in zip(spans, spans[1:]):
+        assert a1 <= b0
+    assert all(s % 256 == 0 for s, _ in spans)
+    assert spans[-1][1] <= i.workspace_bytes
+
+
+def test_enqueue_calls_validate_before_touching_the_gpu():
+    p = da2.da2_plan(_cfg())
+    lib = da2._lib
+    fake = 1 << 20     # aligned, never dereferenced: every call below fails validation first
+    assert lib.da2_prepare(None, fake, fake, fake, fake, 1 << 40, None) == da2.DA2_ERR_INVALID_ARG
+    assert lib.da2_prepare(p.handle, None, fake, fake, fake, 1 << 40, None) == da2.DA2_ERR_INVALID_ARG
+    assert lib.da2_prepare(p.handle, fake, fake, fake, fake + 16, 1 << 40, None) == da2.DA2_ERR_WORKSPACE
+    assert lib.da2_prepare(p.handle, fake, fake, fake, fake, 100, None) == da2.DA2_ERR_WORKSPACE
+    assert lib.da2_attention(p.handle, fake, 100, fake, None) == da2.DA2_ERR_WORKSPACE
+    assert lib.da2_attention(p.handle, fake, 1 << 40, None, None) == da2.DA2_ERR_INVALID_ARG
+    assert lib.da2_set_labels(p.handle, fake, 1 << 40, None, None) == da2.DA2_ERR_INVALID_ARG
+    assert lib.da2_plan_info(None, None) == da2.DA2_ERR_INVALID_ARG
+    lib.da2_plan_destroy(None)
+    for s in range(5):
+        assert da2.status_string(s)
+    assert da2.status_string(99) == "unknown status"

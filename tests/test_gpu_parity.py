@@ -1,0 +1,117 @@
+"""GPU parity through the C ABI against the CPU oracle (MI355X only).
+
+Bars: quantized codes, scales and (outside the 1e-5 exemption band) labels
+bit-exact; pooled values and block scores to float64 rounding; outputs within
+2e-3 max-abs of the oracle on the same quantized operands, with the oracle's
+labels injected and end to end.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+from oracle import draft as D
+from oracle import pipeline as P
+
+from gpu_cases import OUT_TOL, GpuRun, block_rows, check_prepare, compare_outputs, np64, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def da2():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import block_sparse_mixed_amd as m
+    return m
+
+
+def _full_parity(da2, w, heads=None, att_blocks=None):
+    run = GpuRun(da2, w)
+    heads = range(run.bh) if heads is None else heads
+    states = {bh: run.oracle_head(bh) for bh in heads}
+    for bh, st in states.items():
+        say(f"check prepare {w.name} bh={bh}")
+        check_prepare(run, bh, st)
+    # attention with the oracle's own labels injected
+    labels = np.zeros((run.bh, run.nb, run.nb), dtype=np.int8)
+    full_labels = {bh: st.labels for bh, st in states.items()}
+    gpu_lab = run.sec("labels", torch.int8, (run.bh, run.nb, run.nb))
+    for bh in range(run.bh):
+        labels[bh] = full_labels.get(bh, gpu_lab[bh])
+    assert run.set_labels(labels) == 0
+    out = np64(run.attend().reshape(run.bh, w.tokens, w.head_dim))
+    for bh, st in states.items():
+        blocks = range(run.nb) if att_blocks is None else att_blocks
+        want = P.attention_raster(st, blocks=blocks)
+        rows = block_rows(st, blocks)
+        worst, nbad = compare_outputs(out[bh], want, rows)
+        assert worst <= OUT_TOL, f"{w.name} bh={bh}: max |gpu - oracle| = {worst}"
+    return run, states, out
+
+
+def test_tiny_full(da2):
+    _full_parity(da2, S.TINY)
+
+
+def test_small_full(da2):
+    _full_parity(da2, S.SMALL)
+
+
+def test_end_to_end_small_and_determinism(da2):
+    w = S.SMALL
+    run = GpuRun(da2, w)
+    out1 = run.attend()
+    out2 = run.attend()
+    assert torch.equal(out1, out2), "two launches differ"
+    lab = run.sec("labels", torch.int8, (run.bh, run.nb, run.nb))
+    o = np64(out1.reshape(run.bh, w.tokens, w.head_dim))
+    for bh in range(run.bh):
+        st = run.oracle_head(bh)
+        same = np.flatnonzero((lab[bh] == st.labels).all(axis=1))
+        want = P.attention_raster(st, blocks=same)
+        worst, _ = compare_outputs(o[bh], want, block_rows(st, same))
+        assert worst <= OUT_TOL
+
+
+def test_bf16_output_is_rne_of_fp32(da2):
+    w = S.SMALL
+    run = GpuRun(da2, w)
+    o32 = run.attend(out_fp32=True)
+    cfg_bf = da2.make_config(w.batch, w.heads, w.frames, w.grid_h, w.grid_w, w.head_dim, w.win_h, w.win_w,
+                             w.budget_hi, w.budget_lo, out_dtype=da2.DA2_OUT_BF16)
+    plan_bf = da2.da2_plan(cfg_bf)
+    o16 = torch.empty(w.batch, w.heads, w.tokens, w.head_dim, dtype=torch.bfloat16, device="cuda")
+    say("da2_attention bf16 small")
+    da2.da2_attention(plan_bf, run.ws, o16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
+def test_wan_shape_sampled(da2):
+    # full-size launch; codes/labels for two heads, outputs on sampled query
+    # blocks including the partial edge windows (3, 15) and a frame boundary
+    _full_parity(da2, S.WAN480, heads=[0, 7], att_blocks=[0, 3, 15, 16, 170, 335])
+
+
+@pytest.mark.parametrize("hi,lo", [(0.05, 0.0), (0.25, 0.4), (1.0, 0.0), (0.0, 1.0)])
+def test_wan_sweep_points_sampled(da2, hi, lo):
+    w = S.with_budgets(S.WAN480, hi, lo)
+    _full_parity(da2, w, heads=[3], att_blocks=[0, 15, 200])
+
+
+def test_edge_shapes(da2):
+    # one frame smaller than a window; odd sizes; head_dim 64 with 128-token windows
+    cases = [
+        dataclasses.replace(S.TINY, name="subwindow", frames=1, grid_h=5, grid_w=7, win_h=8, win_w=16,
+                            budget_hi=1.0, budget_lo=0.0),
+        dataclasses.replace(S.TINY, name="ragged", frames=3, grid_h=13, grid_w=21, win_h=8, win_w=16,
+                            head_dim=128, budget_hi=0.2, budget_lo=0.4),
+        dataclasses.replace(S.TINY, name="d64w128", frames=2, grid_h=16, grid_w=32, win_h=8, win_w=16,
+                            head_dim=64, budget_hi=0.25, budget_lo=0.5),
+        dataclasses.replace(S.TINY, name="batch2", batch=2, heads=3, frames=2, grid_h=8, grid_w=8),
+    ]
+    for w in cases:
+        _full_parity(da2, w)
