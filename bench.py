@@ -1,0 +1,183 @@
+"""Benchmark of the DraftAttention2 hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+da2_prepare (fused operand preparation + draft map + shared ranking) and
+da2_attention (phased block-sparse attention), on the Wan-480p-shaped
+workload (12 heads, 21 x 30 x 52 latent tokens, d = 128, 8x16 windows,
+budgets 15 % fp8 / 35 % MXFP4 / 50 % skip). Inputs are resident in HBM
+before the timed region.
+
+Prints one JSON line. `value` is the dense-equivalent attention throughput of
+the whole step, 4*B*H*N^2*d / step time. The `roofline` object is for the
+attention kernel (the dominant one): executed (algorithmic) MFMA flops per
+launch over its average launch time, against the blended fp8/MXFP4 peak of
+the step's hi/lo mix, T* = F_hi / P_fp8 + F_lo / P_fp4.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan480p]
+       [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+P_FP8 = 5.0e15       # MI355X dense fp8 MFMA, FLOP/s (published)
+P_FP4 = 10.1e15      # MI355X dense fp4 MFMA, FLOP/s (published)
+P_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s (published)
+METRIC = "dense-equiv attention TFLOPS + % blended MFMA roofline (Wan-480p shape)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan480p")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-blocks", type=int, default=12)
+    return ap.parse_args()
+
+
+def flops(w, nb, n_hi, n_lo):
+    B, H, N, d = w.batch, w.heads, w.tokens, w.head_dim
+    dense = 4.0 * B * H * N * N * d
+    tile = 128.0
+    f_hi = 4.0 * B * H * nb * n_hi * tile * tile * d
+    f_lo = 4.0 * B * H * nb * n_lo * tile * tile * d
+    return dense, f_hi, f_lo
+
+
+def cpu_baseline(w, q, k, v, n_blocks_sample):
+    """The oracle as it stands, single-threaded BLAS, on a bounded sample:
+    one head's full preparation (geometry, pooling, draft map, ranking,
+    quantization) plus attention for a few query blocks; extrapolated to the
+    whole workload in the metric's unit."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import pipeline as P
+    with threadpool_limits(limits=1):
+        f = lambda t: t[0, 0].float().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        st = P.prepare_head(w, f(q), f(k), f(v))
+        t_prep = time.perf_counter() - t0
+        nb = st.geo.n_blocks
+        blocks = [int(b) for b in np.linspace(0, nb - 1, n_blocks_sample).round()]
+        t0 = time.perf_counter()
+        P.attention_raster(st, blocks=blocks)
+        t_att = (time.perf_counter() - t0) / len(blocks)
+    per_head = t_prep + t_att * nb
+    total = per_head * w.batch * w.heads
+    dense, _, _ = flops(w, nb, st.n_hi, st.n_lo)
+    return {
+        "value": dense / total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"head 0 of {w.batch * w.heads}: full preparation ({t_prep:.1f} s) + attention for "
+                   f"{len(blocks)} of {nb} query blocks ({t_att:.2f} s each); extrapolated to all blocks and "
+                   f"heads: {total:.0f} s per step"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over heads with no communication; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_sparse_mixed_amd as da2
+    import synthetic as S
+
+    w = S.WORKLOADS[args.workload]
+    q, k, v = S.make_qkv(w)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, q, k, v, args.cpu_sample_blocks)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    cfg = da2.make_config(w.batch, w.heads, w.frames, w.grid_h, w.grid_w, w.head_dim, w.win_h, w.win_w,
+                          w.budget_hi, w.budget_lo, out_dtype=da2.DA2_OUT_BF16)
+    plan = da2.da2_plan(cfg)
+    info = plan.info
+    ws = plan.workspace(dev)
+    out = torch.empty(w.batch, w.heads, w.tokens, w.head_dim, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        da2.da2_prepare(plan, qd, kd, vd, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        da2.da2_attention(plan, ws, out, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prep_ms = [e[0].elapsed_time(e[1]) for e in events]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in events]
+    step_ms = [e[0].elapsed_time(e[2]) for e in events]
+    ms_per_step = wall * 1e3 / args.steps
+    dense, f_hi, f_lo = flops(w, info.n_blocks, info.n_hi, info.n_lo)
+    t_star = f_hi / P_FP8 + f_lo / P_FP4
+    blended_peak = (f_hi + f_lo) / t_star
+    attn_avg_s = sum(attn_ms) / len(attn_ms) / 1e3
+    achieved = (f_hi + f_lo) / attn_avg_s
+    # the instructions actually issued: half of F_hi (QK^T) on bf16 MFMAs
+    t_star_instr = 0.5 * f_hi / P_BF16 + 0.5 * f_hi / P_FP8 + f_lo / P_FP4
+    res = {
+        "metric": METRIC,
+        "value": dense / (ms_per_step / 1e3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8+mxfp4",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "frames": w.frames,
+                   "grid": [w.grid_h, w.grid_w], "tokens": w.tokens, "head_dim": w.head_dim,
+                   "window": [w.win_h, w.win_w], "budget_hi": w.budget_hi, "budget_lo": w.budget_lo,
+                   "n_blocks": info.n_blocks, "n_hi": info.n_hi, "n_lo": info.n_lo, "out_dtype": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": blended_peak / 1e12, "unit": "TFLOP/s",
+                     "frac": achieved / blended_peak, "traffic": None},
+        "cpu_baseline": cpu,
+        "attention_ms": sum(attn_ms) / len(attn_ms),
+        "attention_ms_min": min(attn_ms),
+        "prepare_ms": sum(prep_ms) / len(prep_ms),
+        "step_ms_events": sum(step_ms) / len(step_ms),
+        "attention_dense_equiv_tflops": dense / attn_avg_s / 1e12,
+        "attention_executed_tflops": achieved / 1e12,
+        "blended_roofline_ms": t_star * 1e3,
+        "issued_mix_roofline_ms": t_star_instr * 1e3,
+        "flops": {"dense_equiv": dense, "f_hi": f_hi, "f_lo": f_lo},
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -101,6 +101,7 @@ extern "C" da2_status da2_plan(const da2_config* cfg, da2_plan_t** out) {
     L.hi = take(B * N * (uint64_t)(g.n_hi > 0 ? g.n_hi : 1) * 4);
     L.lo = take(B * N * (uint64_t)(g.n_lo > 0 ? g.n_lo : 1) * 4);
     L.status = take(16);
+    L.bias = take(N * T * 4);
     L.total = off;
 
     da2_plan_t* p = new (std::nothrow) da2_plan_t;
@@ -147,6 +148,7 @@ extern "C" da2_status da2_plan_info(const da2_plan_t* plan, da2_plan_info_t* out
     i.off_status = L.status;
     i.off_qb = L.qb;
     i.off_kb = L.kb;
+    i.off_bias = L.bias;
     *out = i;
     return DA2_OK;
 }

@@ -99,6 +99,7 @@ typedef struct da2_plan_s da2_plan_t;
  *   hi, lo  i32 [BH][NB][n_hi], [BH][NB][n_lo]  ascending key-block indices
  *   status  u32 [4]             [0]: rows whose labels had the wrong counts
  *                               (written by da2_set_labels)
+ *   bias    f32 [NB][T]         0 for a slot holding a token, -inf for a padded slot
  */
 typedef struct da2_plan_info_s {
     int32_t n_blocks;
@@ -114,7 +115,7 @@ typedef struct da2_plan_info_s {
     uint64_t off_pool, off_q8, off_k8, off_v8t, off_e8;
     uint64_t off_q4, off_k4, off_v4t, off_sq4, off_sk4, off_sv4t;
     uint64_t off_scores, off_labels, off_hi, off_lo, off_status;
-    uint64_t off_qb, off_kb;
+    uint64_t off_qb, off_kb, off_bias;
 } da2_plan_info_t;
 
 /* Validate cfg and build a plan. Host only: touches no GPU state.
