@@ -103,36 +103,46 @@ struct Tile {
 };
 
 // Each wave moves whole 1 KiB rows of 64 x 16 bytes; lane l lands at row + 16 l.
-// The gather order applies the LDS swizzle.
-__device__ __forceinline__ void dma_tile_hi(const Tile& t, uint8_t* buf, int w, int lane) {
-    // 32 KiB bf16 K (32 rows), 16 KiB V (16 rows), 512 B bias (half a row)
+// The gather offsets apply the LDS swizzle; for every row they reduce to a
+// per-lane constant, XORed with a row-uniform bit (checked exhaustively
+// against the swizzle functions above when they were derived).
+struct DmaOffsets {
+    uint32_t k8, k8x, v8, k4, k4x, v4;
+};
+
+__device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
+    DmaOffsets o;
+    o.k8 = ((lane >> 4) << 8) + (((lane & 15) ^ ((lane >> 4) & 3)) << 4);
+    o.k8x = o.k8 ^ 64u;
+    o.v8 = ((lane >> 3) << 7) + (((lane & 7) ^ (lane >> 3)) << 4);
+    o.k4 = ((lane >> 2) << 6) + (((lane & 3) ^ ((lane >> 3) & 1)) << 4);
+    o.k4x = o.k4 ^ 32u;
+    o.v4 = ((lane >> 2) << 6) + (((lane & 3) ^ ((lane >> 3) & 3)) << 4);
+    return o;
+}
+
+__device__ __forceinline__ void dma_tile_hi(const Tile& t, uint8_t* buf, int w, int lane, const DmaOffsets& o) {
+    // 32 KiB bf16 K (rows 0..31), 16 KiB V (rows 32..47), 512 B bias (half a row)
 #pragma unroll
     for (int n = 0; n < 12; ++n) {
-        const int wr = w * 12 + n;           // 0..47
-        if (wr < 32) {
-            const int p = wr * 64 + lane;
-            const int row = p >> 4, pc = p & 15;
-            dma16(t.k + (row * 16 + (pc ^ swz_k8(row))) * 16, buf + kHiK + wr * 1024);
-        } else {
-            const int p = (wr - 32) * 64 + lane;
-            const int row = p >> 3, pc = p & 7;
-            dma16(t.v + (row * 8 + (pc ^ swz_v8(row))) * 16, buf + kHiV + (wr - 32) * 1024);
-        }
+        const int wr = w * 12 + n;
+        if (wr < 32)
+            dma16(t.k + wr * 1024 + ((wr & 4) ? o.k8x : o.k8), buf + kHiK + wr * 1024);
+        else
+            dma16(t.v + (wr - 32) * 1024 + o.v8, buf + kHiV + (wr - 32) * 1024);
     }
     if (w == 0 && lane < 32) dma16(reinterpret_cast<const uint8_t*>(t.bias) + lane * 16, buf + kBias);
 }
 
-__device__ __forceinline__ void dma_tile_lo(const Tile& t, uint8_t* buf, int w, int lane) {
-    // 8 KiB K (8 rows), 8 KiB V (8 rows), scales 2 x 512 B (1 row), bias (half a row)
+__device__ __forceinline__ void dma_tile_lo(const Tile& t, uint8_t* buf, int w, int lane, const DmaOffsets& o) {
+    // 8 KiB K (rows 0..7), 8 KiB V (rows 8..15), scales 2 x 512 B, bias
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-        const int wr = w + 4 * n;            // 0..15
-        const int p = (wr & 7) * 64 + lane;
-        const int row = p >> 2, pc = p & 3;
+        const int wr = w + 4 * n;
         if (wr < 8)
-            dma16(t.k + (row * 4 + (pc ^ swz_k4(row))) * 16, buf + kLoK + wr * 1024);
+            dma16(t.k + wr * 1024 + ((wr & 2) ? o.k4x : o.k4), buf + kLoK + wr * 1024);
         else
-            dma16(t.v + (row * 4 + (pc ^ swz_v4(row))) * 16, buf + kLoV + (wr - 8) * 1024);
+            dma16(t.v + (wr - 8) * 1024 + o.v4, buf + kLoV + (wr - 8) * 1024);
     }
     if (w == 1) dma16(lane < 32 ? t.ks + lane * 16 : t.vs + (lane - 32) * 16, buf + kLoS);
     if (w == 2 && lane < 32) dma16(reinterpret_cast<const uint8_t*>(t.bias) + lane * 16, buf + kBias);
@@ -247,6 +257,19 @@ __device__ __forceinline__ void step(WaveState& st, const uint8_t* cur, const ui
             psc[u] = min(254, max(0, scl));
         }
     }
+    // rescale when the running max grew (rare: tiles arrive best-ranked first);
+    // done before the exponentials so that nothing gets sunk below a branch
+    if (mnew[0] > st.m[0] || mnew[1] > st.m[1]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const float f = exp2f(st.m[u] - mnew[u]);
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) st.acc[u][ct] *= f;
+            st.lsum[u] *= f;
+        }
+    }
+    st.m[0] = mnew[0];
+    st.m[1] = mnew[1];
     v8i pop[2];
     KOp ko[2];
     if constexpr (PN != kNone) load_kop<PN>(ko[0], nxt, 0, r, g4);
@@ -289,18 +312,6 @@ __device__ __forceinline__ void step(WaveState& st, const uint8_t* cur, const ui
             pop[u][4] = 0; pop[u][5] = 0; pop[u][6] = 0; pop[u][7] = 0;
         }
     }
-    // rescale when the running max grew (rare after the first tiles)
-    if (mnew[0] > st.m[0] || mnew[1] > st.m[1]) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const float f = exp2f(st.m[u] - mnew[u]);
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct) st.acc[u][ct] *= f;
-            st.lsum[u] *= f;
-        }
-    }
-    st.m[0] = mnew[0];
-    st.m[1] = mnew[1];
     // O^T += V^T . P^T and l += 1 . P^T
     v8i ones;
 #pragma unroll
@@ -370,11 +381,12 @@ __device__ __forceinline__ Tile tile_at(const AttnArgs& a, int bh, int qb, int i
     return t;
 }
 
-__device__ __forceinline__ void dma_tile(const AttnArgs& a, const Tile& t, int idx, uint8_t* buf, int w, int lane) {
+__device__ __forceinline__ void dma_tile(const AttnArgs& a, const Tile& t, int idx, uint8_t* buf, int w, int lane,
+                                         const DmaOffsets& o) {
     if (idx < a.g.n_hi)
-        dma_tile_hi(t, buf, w, lane);
+        dma_tile_hi(t, buf, w, lane, o);
     else
-        dma_tile_lo(t, buf, w, lane);
+        dma_tile_lo(t, buf, w, lane, o);
 }
 
 }  // namespace
@@ -403,13 +415,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const uint64_t qtile = (uint64_t)bh * nb + qb;
     const int n_tiles = g.n_hi + g.n_lo;
 
+    const DmaOffsets doff = dma_offsets(lane);
     // start the first two tiles' DMA before touching Q
     const Tile t0 = tile_at(a, bh, qb, 0);
-    dma_tile(a, t0, 0, lds, w, lane);
+    dma_tile(a, t0, 0, lds, w, lane, doff);
     Tile t1 = t0;
     if (n_tiles > 1) {
         t1 = tile_at(a, bh, qb, 1);
-        dma_tile(a, t1, 1, lds + kBufBytes, w, lane);
+        dma_tile(a, t1, 1, lds + kBufBytes, w, lane, doff);
     }
 
     WaveState st;
@@ -450,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         Tile t2 = nxt;
         if (idx + 2 < n_tiles) {
             t2 = tile_at(a, bh, qb, idx + 2);
-            dma_tile(a, t2, idx + 2, lds + ((idx + 2) % 3) * kBufBytes, w, lane);
+            dma_tile(a, t2, idx + 2, lds + ((idx + 2) % 3) * kBufBytes, w, lane, doff);
         }
         return t2;
     };

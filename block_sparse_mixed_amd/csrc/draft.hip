@@ -18,8 +18,9 @@
 //   rank_kernel         : per (bh, query block i): row softmax of both maps,
 //                         C = (A_avg + A_max) / 2, bitonic sort on
 //                         (C descending, index ascending), labels, and the
-//                         ascending hi/lo index lists by ballot compaction.
-//   set_labels_kernel   : test hook; lists from given labels, count check.
+//                         hi/lo index lists in that rank order.
+//   set_labels_kernel   : test hook; ascending lists from given labels by
+//                         ballot compaction, count check.
 #include "common.hpp"
 
 namespace da2 {
@@ -185,10 +186,14 @@ __global__ __launch_bounds__(256) void rank_kernel(Geo g, double* __restrict__ s
     __syncthreads();
     int8_t* lrow = labels + ((uint64_t)bh * nb + i) * nb;
     for (int j = tid; j < nb; j += 256) lrow[j] = lab[j];
-    if (tid < 64) {
-        const uint64_t rowid = (uint64_t)bh * nb + i;
-        if (g.n_hi > 0) compact_list(lab, nb, DA2_HI, hi_list + rowid * g.n_hi, g.n_hi);
-        if (g.n_lo > 0) compact_list(lab, nb, DA2_LO, lo_list + rowid * g.n_lo, g.n_lo);
+    // lists in rank order (best first): the attention kernel then meets each
+    // row's largest scores early and rarely has to rescale its accumulator
+    const uint64_t rowid = (uint64_t)bh * nb + i;
+    for (int r = tid; r < n_ret; r += 256) {
+        if (r < g.n_hi)
+            hi_list[rowid * g.n_hi + r] = idx[r];
+        else
+            lo_list[rowid * g.n_lo + (r - g.n_hi)] = idx[r];
     }
 }
 

@@ -96,7 +96,9 @@ typedef struct da2_plan_s da2_plan_t;
  *   scores  f64 [2][BH][NB][NB] draft logits; after da2_prepare section 0 holds
  *                               the combined block score C
  *   labels  i8  [BH][NB][NB]   DA2_SKIP / DA2_LO / DA2_HI
- *   hi, lo  i32 [BH][NB][n_hi], [BH][NB][n_lo]  ascending key-block indices
+ *   hi, lo  i32 [BH][NB][n_hi], [BH][NB][n_lo]  key-block indices: in rank order
+ *                               (best first) after da2_prepare, ascending after
+ *                               da2_set_labels
  *   status  u32 [4]             [0]: rows whose labels had the wrong counts
  *                               (written by da2_set_labels)
  *   bias    f32 [NB][T]         0 for a slot holding a token, -inf for a padded slot

@@ -120,14 +120,15 @@ def check_prepare(run: GpuRun, bh: int, st: P.HeadState):
     if diff.any():
         ex = D.exemption_mask(st.scores, n_hi, n_lo)
         assert not (diff & ~ex).any(), "labels differ outside the exemption band"
-    if n_hi:
-        hi = run.sec("hi", torch.int32, (BH, nb, n_hi))[bh]
+    # lists: the labelled blocks in rank order (the GPU's own C descending, lower index first)
+    for name, lv, n in (("hi", D.HI, n_hi), ("lo", D.LO, n_lo)):
+        if not n:
+            continue
+        lst = run.sec(name, torch.int32, (BH, nb, n))[bh]
         for i in range(nb):
-            assert np.array_equal(hi[i], np.flatnonzero(lab[i] == D.HI))
-    if n_lo:
-        lo = run.sec("lo", torch.int32, (BH, nb, n_lo))[bh]
-        for i in range(nb):
-            assert np.array_equal(lo[i], np.flatnonzero(lab[i] == D.LO))
+            members = np.flatnonzero(lab[i] == lv)
+            want = sorted(members, key=lambda j: (-C[i, j], j))
+            assert list(lst[i]) == want, f"{name} list of row {i}"
     return lab
 
 
