@@ -13,13 +13,23 @@ attention kernel (the dominant one): executed (algorithmic) MFMA flops per
 launch over its average launch time, against the blended fp8/MXFP4 peak of
 the step's hi/lo mix, T* = F_hi / P_fp8 + F_lo / P_fp4.
 
+The `traffic` field is the attention kernel's HBM bytes per launch from the
+FETCH_SIZE and WRITE_SIZE counters (rocprofv3 --pmc), each scaled by what the
+same counter reads for a plain streaming kernel of known size
+(`--copy-calibration`). Those figures are kept in
+profiles/attn_wan480p_traffic.md together with the SHA-256 of the attention
+kernel's source they were taken on; when the source has changed since, the
+field is null.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan480p]
        [--no-cpu-baseline]
+       python bench.py --copy-calibration   (counter calibration run only)
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -44,7 +54,52 @@ def parse():
     ap.add_argument("--workload", default="wan480p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=12)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a streaming kernel of known size (read 1 GiB, write 1 GiB), for counter scaling")
     return ap.parse_args()
+
+
+ATTN_SOURCE = os.path.join(HERE, "block_sparse_mixed_amd", "csrc", "attn.hip")
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "attn_wan480p_traffic.md")
+
+
+def attn_source_sha256():
+    with open(ATTN_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def recorded_traffic(workload):
+    """Scaled HBM bytes per attention launch from the committed counter summary,
+    or None when it is missing, for another workload, or for other kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ":" in line:
+            key, val = line[2:].split(":", 1)
+            fields[key.strip()] = val.strip().strip("`")
+    if fields.get("workload") != workload or fields.get("attn_source_sha256") != attn_source_sha256():
+        return None
+    try:
+        return float(fields["scaled_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28                     # 2^28 fp32 = 1 GiB read + 1 GiB written per launch
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"kernel": "torch.mul(src, 1.0, out=dst)", "read_bytes": 4 * n,
+                                           "write_bytes": 4 * n, "launches": 3}}), flush=True)
 
 
 def flops(w, nb, n_hi, n_lo):
@@ -91,6 +146,9 @@ def cpu_baseline(w, q, k, v, n_blocks_sample):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards over heads with no communication; see the design notes).", file=sys.stderr)
@@ -164,7 +222,7 @@ def main():
                    "window": [w.win_h, w.win_w], "budget_hi": w.budget_hi, "budget_lo": w.budget_lo,
                    "n_blocks": info.n_blocks, "n_hi": info.n_hi, "n_lo": info.n_lo, "out_dtype": "bf16"},
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": blended_peak / 1e12, "unit": "TFLOP/s",
-                     "frac": achieved / blended_peak, "traffic": None},
+                     "frac": achieved / blended_peak, "traffic": recorded_traffic(w.name)},
         "cpu_baseline": cpu,
         "attention_ms": sum(attn_ms) / len(attn_ms),
         "attention_ms_min": min(attn_ms),

@@ -2,8 +2,10 @@
 
 Argument marshalling only: every step of the path runs in the library's HIP
 kernels. torch tensors supply device pointers and the current stream. The
-functions mirror the C ABI in include/da2.h; importing this module fails loudly
-when the library has not been built.
+functions mirror the C ABI in include/da2.h. The library is loaded on first
+use (so that the build step can import this package before it exists); that
+first call fails loudly when the library has not been built. There is no
+fallback of any kind.
 """
 
 from __future__ import annotations
@@ -23,7 +25,12 @@ DPAD = 128
 
 class Da2Error(RuntimeError):
     def __init__(self, status: int, where: str):
-        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        msg = f"{where}: {status_string(status)} (status {status})"
+        if status == DA2_ERR_HIP:
+            name = ctypes.c_char_p()
+            code = _lib.da2_last_hip_error(ctypes.byref(name))
+            msg += f": {name.value.decode()} ({code})"
+        super().__init__(msg)
         self.status = status
 
 
@@ -54,7 +61,7 @@ class PlanInfo(ctypes.Structure):
 
 
 EXPORTS = ("da2_plan", "da2_plan_destroy", "da2_plan_info", "da2_prepare", "da2_attention",
-           "da2_set_labels", "da2_status_string")
+           "da2_set_labels", "da2_status_string", "da2_last_hip_error")
 
 
 def _load():
@@ -76,10 +83,22 @@ def _load():
     lib.da2_set_labels.restype = ctypes.c_int
     lib.da2_status_string.argtypes = [ctypes.c_int]
     lib.da2_status_string.restype = ctypes.c_char_p
+    lib.da2_last_hip_error.argtypes = [ctypes.POINTER(ctypes.c_char_p)]
+    lib.da2_last_hip_error.restype = ctypes.c_int
     return lib
 
 
-_lib = _load()
+class _LazyLib:
+    """libda2, opened on first attribute access."""
+    _cdll = None
+
+    def __getattr__(self, name):
+        if _LazyLib._cdll is None:
+            _LazyLib._cdll = _load()
+        return getattr(_LazyLib._cdll, name)
+
+
+_lib = _LazyLib()
 
 
 def status_string(status: int) -> str:

@@ -24,6 +24,14 @@ da2_status check_ws(const da2_plan_t* plan, const void* ws, size_t bytes) {
     return DA2_OK;
 }
 
+// The HIP error behind the last DA2_ERR_HIP of this thread.
+thread_local hipError_t g_last_hip = hipSuccess;
+
+da2_status hip_fail(hipError_t e) {
+    g_last_hip = e;
+    return DA2_ERR_HIP;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // 16-byte vector loads/stores of rows need 8-element alignment of the strides.
@@ -40,8 +48,9 @@ extern "C" da2_status da2_prepare(const da2_plan_t* plan, const void* q, const v
     if (st != DA2_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !strides_vectorizable(plan->geo)) return DA2_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    if (da2::launch_prep(plan->geo, plan->ws, q, k, v, workspace, s) != hipSuccess) return DA2_ERR_HIP;
-    if (da2::launch_draft(plan->geo, plan->ws, workspace, s) != hipSuccess) return DA2_ERR_HIP;
+    if (hipError_t e = da2::launch_prep(plan->geo, plan->ws, q, k, v, workspace, s); e != hipSuccess)
+        return hip_fail(e);
+    if (hipError_t e = da2::launch_draft(plan->geo, plan->ws, workspace, s); e != hipSuccess) return hip_fail(e);
     return DA2_OK;
 }
 
@@ -52,8 +61,9 @@ extern "C" da2_status da2_attention(const da2_plan_t* plan, const void* workspac
     if (st != DA2_OK) return st;
     if (!aligned16(out) || !strides_vectorizable(plan->geo)) return DA2_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    if (da2::launch_attention(plan->geo, plan->ws, workspace, out, plan->cfg.out_dtype == DA2_OUT_FP32, s) != hipSuccess)
-        return DA2_ERR_HIP;
+    const int out_fp32 = plan->cfg.out_dtype == DA2_OUT_FP32;
+    if (hipError_t e = da2::launch_attention(plan->geo, plan->ws, workspace, out, out_fp32, s); e != hipSuccess)
+        return hip_fail(e);
     return DA2_OK;
 }
 
@@ -63,6 +73,12 @@ extern "C" da2_status da2_set_labels(const da2_plan_t* plan, void* workspace, si
     da2_status st = check_ws(plan, workspace, workspace_bytes);
     if (st != DA2_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    if (da2::launch_set_labels(plan->geo, plan->ws, workspace, labels_dev, s) != hipSuccess) return DA2_ERR_HIP;
+    if (hipError_t e = da2::launch_set_labels(plan->geo, plan->ws, workspace, labels_dev, s); e != hipSuccess)
+        return hip_fail(e);
     return DA2_OK;
+}
+
+extern "C" int da2_last_hip_error(const char** name) {
+    if (name) *name = hipGetErrorName(g_last_hip);
+    return static_cast<int>(g_last_hip);
 }

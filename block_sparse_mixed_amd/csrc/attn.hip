@@ -543,8 +543,7 @@ hipError_t launch_attention(const Geo& g, const Layout& L, const void* ws, void*
     a.out = out;
     a.out_fp32 = out_fp32;
     const int total = g.bh * g.n_blocks;
-    hipLaunchKernelGGL(attn_kernel, dim3(total), dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
+    return launch_kernel(attn_kernel, dim3(total), dim3(kThreads), 0, stream, a);
 }
 
 }  // namespace da2

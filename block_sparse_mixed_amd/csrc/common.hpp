@@ -5,10 +5,27 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <tuple>
+#include <utility>
 
 #include "da2_internal.hpp"
 
 namespace da2 {
+
+// Launch a kernel and return the error of this launch alone. (The "last
+// error" of the runtime also holds failures of unrelated earlier calls made
+// by other code in the process, so it is not consulted.)
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                         A&&... args) {
+    std::tuple<P...> vals(std::forward<A>(args)...);
+    return std::apply(
+        [&](auto&... v) {
+            void* ptrs[] = {static_cast<void*>(&v)...};
+            return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shmem, stream);
+        },
+        vals);
+}
 
 // Window (block) position of block index blk: (frame, window row, window column).
 struct BlockPos {

@@ -224,13 +224,12 @@ hipError_t launch_draft(const Geo& g, const Layout& L, void* ws, hipStream_t str
     const double* pool = reinterpret_cast<const double*>(base + L.pool);
     double* scores = reinterpret_cast<double*>(base + L.scores);
     const int t = (g.n_blocks + kTile - 1) / kTile;
-    hipLaunchKernelGGL(draft_logits_kernel, dim3(t, t, 2 * g.bh), dim3(256), 0, stream, g, pool, scores);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_kernel(draft_logits_kernel, dim3(t, t, 2 * g.bh), dim3(256), 0, stream, g, pool, scores);
     if (e != hipSuccess) return e;
     int np = 1;
     while (np < g.n_blocks) np <<= 1;
     const size_t shmem = (size_t)np * (8 + 4 + 1);
-    hipLaunchKernelGGL(rank_kernel, dim3(g.n_blocks, g.bh), dim3(256), shmem, stream, g, scores,
+    return launch_kernel(rank_kernel, dim3(g.n_blocks, g.bh), dim3(256), shmem, stream, g, scores,
                        reinterpret_cast<int8_t*>(base + L.labels), reinterpret_cast<int32_t*>(base + L.hi),
                        reinterpret_cast<int32_t*>(base + L.lo));
     return hipGetLastError();
@@ -239,10 +238,9 @@ hipError_t launch_draft(const Geo& g, const Layout& L, void* ws, hipStream_t str
 hipError_t launch_set_labels(const Geo& g, const Layout& L, void* ws, const int8_t* labels, hipStream_t stream) {
     uint8_t* base = static_cast<uint8_t*>(ws);
     uint32_t* status = reinterpret_cast<uint32_t*>(base + L.status);
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, status, 4);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_kernel(zero_u32_kernel, dim3(1), dim3(64), 0, stream, status, 4);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(set_labels_kernel, dim3(g.n_blocks, g.bh), dim3(64), 0, stream, g, labels,
+    return launch_kernel(set_labels_kernel, dim3(g.n_blocks, g.bh), dim3(64), 0, stream, g, labels,
                        reinterpret_cast<int8_t*>(base + L.labels), reinterpret_cast<int32_t*>(base + L.hi),
                        reinterpret_cast<int32_t*>(base + L.lo), status);
     return hipGetLastError();

@@ -209,8 +209,7 @@ hipError_t launch_prep(const Geo& g, const Layout& L, const void* q, const void*
     a.src[2] = static_cast<const uint16_t*>(v);
     a.ws = static_cast<uint8_t*>(ws);
     a.L = L;
-    hipLaunchKernelGGL(prep_kernel, dim3(g.n_blocks, g.bh, 3), dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
+    return launch_kernel(prep_kernel, dim3(g.n_blocks, g.bh, 3), dim3(kThreads), 0, stream, a);
 }
 
 }  // namespace da2

@@ -172,6 +172,11 @@ da2_status da2_set_labels(const da2_plan_t* plan, void* workspace, size_t worksp
 /* Static, never-NULL description of a status code. */
 const char* da2_status_string(da2_status status);
 
+/* The HIP error code behind the last DA2_ERR_HIP returned on the calling
+ * thread (0 if none yet), and, when name is not NULL, its static, never-NULL
+ * HIP error name in *name. Does not touch the device. */
+int da2_last_hip_error(const char** name);
+
 #ifdef __cplusplus
 }
 #endif

@@ -129,3 +129,10 @@ def test_enqueue_calls_validate_before_touching_the_gpu():
     for s in range(5):
         assert da2.status_string(s)
     assert da2.status_string(99) == "unknown status"
+
+
+def test_last_hip_error_is_clear_before_any_failure():
+    name = ctypes.c_char_p()
+    assert da2._lib.da2_last_hip_error(ctypes.byref(name)) == 0
+    assert name.value.decode() == "hipSuccess"
+    assert da2._lib.da2_last_hip_error(None) == 0
