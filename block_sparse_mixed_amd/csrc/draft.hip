@@ -232,7 +232,6 @@ hipError_t launch_draft(const Geo& g, const Layout& L, void* ws, hipStream_t str
     return launch_kernel(rank_kernel, dim3(g.n_blocks, g.bh), dim3(256), shmem, stream, g, scores,
                        reinterpret_cast<int8_t*>(base + L.labels), reinterpret_cast<int32_t*>(base + L.hi),
                        reinterpret_cast<int32_t*>(base + L.lo));
-    return hipGetLastError();
 }
 
 hipError_t launch_set_labels(const Geo& g, const Layout& L, void* ws, const int8_t* labels, hipStream_t stream) {
@@ -243,7 +242,6 @@ hipError_t launch_set_labels(const Geo& g, const Layout& L, void* ws, const int8
     return launch_kernel(set_labels_kernel, dim3(g.n_blocks, g.bh), dim3(64), 0, stream, g, labels,
                        reinterpret_cast<int8_t*>(base + L.labels), reinterpret_cast<int32_t*>(base + L.hi),
                        reinterpret_cast<int32_t*>(base + L.lo), status);
-    return hipGetLastError();
 }
 
 }  // namespace da2
