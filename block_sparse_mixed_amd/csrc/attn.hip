@@ -7,32 +7,49 @@
 // (arXiv 2505.14708), abstract]: outputs return to the original token order.
 //
 // Work decomposition (gfx950, wave64):
-//   one workgroup = one query block (128 slots) of one (batch, head); 4 waves,
-//   wave w owns query slots 32w .. 32w+31 as two 16-query tiles u.
-//   The query block's key tiles (hi list, then lo list) stream through three
-//   LDS buffers filled by direct global->LDS DMA two tiles ahead, so one
-//   barrier per tile is the only synchronisation. Per key tile every wave runs
-//     S^T = K . Q^T        fp8 phase: V_MFMA_F32_16X16X32_BF16 on the E4M3
+//   one workgroup = one query block (128 slots) of one (batch, head), eight
+//   waves in two teams of four. Wave w%4 of either team owns query slots
+//   32(w%4) .. +32 as two 16-query tiles u. The query block's key tiles run
+//   as two sections, the hi list and then the lo list (each best-ranked
+//   first), so that every loop body has a single precision. Within a section
+//   the tiles alternate between the teams: team 0 takes tiles 0, 2, 4, ...,
+//   team 1 tiles 1, 3, 5, ...
+//   Time runs in phases separated by workgroup barriers. In phase p the team
+//   owning tile p runs its matrix work, PV of tile p-2 and QK^T of tile p,
+//   while the other team runs the softmax of tile p-1. The two waves sharing
+//   a SIMD are therefore always in opposite halves of their work: one keeps
+//   the MFMA pipe busy while the other exponentiates.
+//     S^T = K . Q^T        fp8 tiles: V_MFMA_F32_16X16X32_BF16 on the E4M3
 //                          values decoded to bf16 (exact);
-//                          MXFP4 phase: V_MFMA_SCALE_F32_16X16X128_F8F6F4
-//     softmax (base 2, integer running max, lane-local rescale)
+//                          MXFP4 tiles: V_MFMA_SCALE_F32_16X16X128_F8F6F4
+//     softmax (base 2, integer running max per team, lane-local rescale)
 //     O^T += V^T . P^T     scaled f8f6f4 MFMAs (E4M3 or E2M1 operands), plus
 //                          one with an all-ones A that yields the row sum
 //                          l = sum P~ in the same lanes as O.
-//   The QK^T of the next tile is issued in the same instruction stream as the
-//   softmax of the current one, so the MFMA pipe works while the VALU
-//   exponentiates. Padded key slots are excluded by starting the QK^T
-//   accumulator at a per-slot bias (0 or -inf) that rides along with the tile.
+//   The query block's Q operands (bf16 and E2M1) sit in LDS for the whole
+//   kernel. K and V^T of a tile travel by direct global->LDS DMA into
+//   separate two-slot pools: K of tile p+1 and V^T of tile p-1 are issued at
+//   the start of phase p. At the end the teams' (max, sum, accumulator) triples merge
+//   exactly: their maxima are integers, so the rescale factors are powers of
+//   two. Padded key slots are excluded by starting the QK^T accumulator at a
+//   per-slot bias (0 or -inf) that travels with K.
 //
 //   Computing S transposed makes each lane hold 32 keys of one query, which
 //   is exactly the B-operand layout of the PV product: P never leaves the
 //   lane, the MXFP4 group of P is the lane's own 32 values, and the max
-//   reduction needs two cross-lane steps (xor 16, xor 32).
+//   reduction needs two cross-lane steps (permlane swaps of 32 and 16 lanes).
 //
-//   The fp8 phase's QK^T runs on bf16 MFMAs because the f8f6f4 MFMA keeps only
+//   Register budget: two waves per SIMD leave 256 registers per wave, of
+//   which the accumulator takes 64 and the scores another 64. The code is
+//   shaped so the allocator needs no copies or spills in the loops: static
+//   slot parity, no precision branches inside a loop body, values derived
+//   from the lane index recomputed where used, E2M1 operands kept as four
+//   dwords, and the rare rescale done in place.
+//
+//   The fp8 tiles' QK^T runs on bf16 MFMAs because the f8f6f4 MFMA keeps only
 //   about 12 bits below its largest product when it sums fp8 products: with
 //   outlier channels the scores move by ~1e-2 (log2 units), enough to flip the
-//   rounding of many P codes. Its PV product stays fp8: nothing is decided
+//   rounding of many P codes. Their PV product stays fp8: nothing is decided
 //   from its rounding.
 //
 // Operand layouts (measured on gfx950): a 16x16x128 fp8 operand lane l holds
@@ -40,15 +57,18 @@
 // lane l holds row l%16 and nibble j -> k = 32*(l/16) + j; the E8M0 scale of
 // lane l belongs to (row l%16, k-block l/16); D lane l element e is
 // D[4*(l/16) + e][l%16]. A 16x16x32 bf16 MFMA only needs A and B to share
-// their lane/k assignment. The key slot fed to A-row r of key tile t is chosen
-// so that P's register order matches the PV k order:
+// their lane/k assignment. The key slot fed to A-row r of key sub-tile t is
+// chosen so that P's register order matches the PV k order:
 //   fp8:  slot = 64*(t/4) + 16*(r/4) + 4*(t%4) + r%4
 //   fp4:  slot = 32*(r/4) + 4*t + r%4          (k-block g = slots 32g..32g+31)
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace da2 {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
@@ -62,21 +82,24 @@ struct AttnArgs {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kFmtFp8 = 0;
 constexpr int kFmtFp4 = 4;
 constexpr float kLog2E = 1.4426950408889634f;
 constexpr float kLog2Six = 2.5849625007211562f;
-constexpr int kHi = 0, kLo = 1, kNone = 2;
+constexpr int kHi = 0, kLo = 1;
 
-// LDS buffer layout (bytes). fp8 phase: bf16 K [128][256] | E4M3 V^T [128][128];
-// MXFP4 phase: E2M1 K [128][64] | E2M1 V^T [128][64] | K scales [128][4] |
-// V scales [128][4]; both: bias f32 [128] at kBias.
-constexpr int kHiK = 0, kHiV = 32768;
-constexpr int kLoK = 0, kLoV = 8192, kLoS = 16384;
-constexpr int kBias = 49152;
-constexpr int kBufBytes = kBias + 512;
-constexpr int kNumBuf = 3;
+// LDS: K slots [K data 32 KiB | bias f32[128] | E8M0 K scales [128][4]] and
+// V slots [V^T data 16 KiB | E8M0 V scales [128][4]], two of each, and Q.
+// fp8 tiles: K data = bf16 [128 slots][256 B], V data = E4M3 [128 ch][128 B];
+// MXFP4 tiles: K data = E2M1 [128 slots][64 B], V data = E2M1 [128 ch][64 B].
+constexpr int kKBias = 32768, kKScale = 33280, kKSlot = 33792;
+constexpr int kVScale = 16384, kVSlot = 16896;
+constexpr int kSlots = 2;
+// Q: bf16 [128][256 B] | E2M1 [128][64 B] | E8M0 [128][4]
+constexpr int kQb = 0, kQ4 = 32768, kQs = 40960, kQBytes = 41472;
+constexpr int kListBytes = 4 * DA2_MAX_BLOCKS;    // packed tile list
+static_assert(2 * 66 * 64 * 4 <= kKSlot, "team merge area: two waves per K slot");
 
 // LDS swizzles (16-byte chunk index XOR a row function) so that the eight
 // lanes served together by a 128-bit LDS read hit distinct banks.
@@ -88,288 +111,79 @@ __device__ __forceinline__ int swz_v4(int c) { return (c >> 1) & 3; }
 __device__ __forceinline__ int slot_fp8(int t, int r) { return 64 * (t >> 2) + 16 * (r >> 2) + 4 * (t & 3) + (r & 3); }
 __device__ __forceinline__ int slot_fp4(int t, int r) { return 32 * (r >> 2) + 4 * t + (r & 3); }
 
+// Keeps an MFMA source operand alive past its last MFMA, so that the register
+// allocator never gives that MFMA a destination overlapping the operand (the
+// hardware still reads sources while a multi-pass MFMA writes its result).
+// The asm statement reads and "rewrites" the operand, so it cannot be
+// scheduled ahead of the MFMAs that read it.
+template <class T>
+__device__ __forceinline__ void keep(T& x) {
+    asm volatile("" : "+v"(x));
+}
+
+// The lane index computed afresh where it is used: the compiler cannot hoist
+// an asm statement out of a loop, so nothing lane-dependent stays live (and
+// spills) across the main loop. Two ALU instructions, no memory access.
+__device__ __forceinline__ int fresh_lane() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
+// Scheduling fence: nothing moves across it, which bounds register live ranges.
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
 __device__ __forceinline__ void dma16(const void* gsrc, uint8_t* ldst) {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
                                      (__attribute__((address_space(3))) void*)ldst, 16, 0, 0);
 }
 
-struct Tile {
-    const uint8_t* k;      // bf16 K (fp8 phase) or E2M1 K
-    const uint8_t* v;      // E4M3 V^T or E2M1 V^T
-    const uint8_t* ks;     // E2M1 K scales (MXFP4 phase)
-    const uint8_t* vs;     // E2M1 V scales (MXFP4 phase)
-    const float* bias;     // per-slot 0 / -inf
-    int e_k, e_v;          // fp8 block exponents (fp8 phase)
-};
-
-// Each wave moves whole 1 KiB rows of 64 x 16 bytes; lane l lands at row + 16 l.
-// The gather offsets apply the LDS swizzle; for every row they reduce to a
-// per-lane constant, XORed with a row-uniform bit (checked exhaustively
-// against the swizzle functions above when they were derived).
+// Per-lane gather offsets of a 1 KiB DMA row that apply the LDS swizzle; for
+// every row they reduce to a per-lane constant, XORed with a row-uniform bit.
 struct DmaOffsets {
-    uint32_t k8, k8x, v8, k4, k4x, v4;
+    uint32_t k8, v8, k4, v4;
 };
 
 __device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
     DmaOffsets o;
     o.k8 = ((lane >> 4) << 8) + (((lane & 15) ^ ((lane >> 4) & 3)) << 4);
-    o.k8x = o.k8 ^ 64u;
     o.v8 = ((lane >> 3) << 7) + (((lane & 7) ^ (lane >> 3)) << 4);
     o.k4 = ((lane >> 2) << 6) + (((lane & 3) ^ ((lane >> 3) & 1)) << 4);
-    o.k4x = o.k4 ^ 32u;
     o.v4 = ((lane >> 2) << 6) + (((lane & 3) ^ ((lane >> 3) & 3)) << 4);
     return o;
 }
 
-__device__ __forceinline__ void dma_tile_hi(const Tile& t, uint8_t* buf, int w, int lane, const DmaOffsets& o) {
-    // 32 KiB bf16 K (rows 0..31), 16 KiB V (rows 32..47), 512 B bias (half a row)
-#pragma unroll
-    for (int n = 0; n < 12; ++n) {
-        const int wr = w * 12 + n;
-        if (wr < 32)
-            dma16(t.k + wr * 1024 + ((wr & 4) ? o.k8x : o.k8), buf + kHiK + wr * 1024);
-        else
-            dma16(t.v + (wr - 32) * 1024 + o.v8, buf + kHiV + (wr - 32) * 1024);
-    }
-    if (w == 0 && lane < 32) dma16(reinterpret_cast<const uint8_t*>(t.bias) + lane * 16, buf + kBias);
-}
-
-__device__ __forceinline__ void dma_tile_lo(const Tile& t, uint8_t* buf, int w, int lane, const DmaOffsets& o) {
-    // 8 KiB K (rows 0..7), 8 KiB V (rows 8..15), scales 2 x 512 B, bias
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int wr = w + 4 * n;
-        if (wr < 8)
-            dma16(t.k + wr * 1024 + ((wr & 2) ? o.k4x : o.k4), buf + kLoK + wr * 1024);
-        else
-            dma16(t.v + (wr - 8) * 1024 + o.v4, buf + kLoV + (wr - 8) * 1024);
-    }
-    if (w == 1) dma16(lane < 32 ? t.ks + lane * 16 : t.vs + (lane - 32) * 16, buf + kLoS);
-    if (w == 2 && lane < 32) dma16(reinterpret_cast<const uint8_t*>(t.bias) + lane * 16, buf + kBias);
-}
-
-struct WaveState {
-    v8bf qb[2][4];         // bf16 Q operands per query tile and k-step
-    v8i q4[2];             // E2M1 Q operands
-    int q4s[2];            // their E8M0 scales
-    v4f acc[2][8];         // O^T: [u][channel tile]; lane holds channels 16ct + 4g + e of query r
-    v4f lsum[2];           // row sums (all four elements equal)
-    float m[2];            // running integer max (log2 units)
-    float c_lo;            // tau * log2(e)
-    float c_hi_q;          // tau * log2(e) * 2^e_q8
+struct Tile {
+    const uint8_t* k;      // bf16 K (fp8 tile) or E2M1 K
+    const uint8_t* v;      // E4M3 V^T or E2M1 V^T
+    const uint8_t* ks;     // E2M1 K scales
+    const uint8_t* vs;     // E2M1 V scales
+    const float* bias;     // per-slot 0 / -inf
+    int hi;                // fp8 tile
+    int e_k, e_v;          // fp8 block exponents
 };
 
-// K operand of key sub-tile t for the QK^T of phase PH, read from LDS.
-struct KOp {
-    v8bf b[4];     // fp8 phase: bf16, one per k-step
-    v8i f;         // MXFP4 phase: E2M1 codes (4 dwords used)
-    v4f bias;
-    int sc;        // MXFP4 phase: E8M0 scale
-};
-
+// The key tile at position idx of the query block's list (hi blocks first),
+// from the packed copy of the list in LDS: block index in bits 0-15, biased
+// K and V fp8 exponents in bits 16-23 and 24-31.
 template <int PH>
-__device__ __forceinline__ void load_kop(KOp& o, const uint8_t* buf, int t, int r, int g4) {
-    const float* bias = reinterpret_cast<const float*>(buf + kBias);
-    if constexpr (PH == kHi) {
-        const int srow = slot_fp8(t, r);
-        const int sw = swz_k8(srow);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            o.b[kk] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(buf + kHiK + srow * 256 + (((4 * kk + g4) ^ sw) << 4)));
-        o.bias = *reinterpret_cast<const v4f*>(bias + slot_fp8(t, 4 * g4));
-    } else {
-        const int srow = slot_fp4(t, r);
-        const uint4 x = *reinterpret_cast<const uint4*>(buf + kLoK + srow * 64 + ((g4 ^ swz_k4(srow)) << 4));
-        o.f[0] = (int)x.x; o.f[1] = (int)x.y; o.f[2] = (int)x.z; o.f[3] = (int)x.w;
-        o.f[4] = 0; o.f[5] = 0; o.f[6] = 0; o.f[7] = 0;
-        o.sc = buf[kLoS + srow * 4 + g4];
-        o.bias = *reinterpret_cast<const v4f*>(bias + slot_fp4(t, 4 * g4));
-    }
-}
-
-template <int PH>
-__device__ __forceinline__ void qk_sub(const WaveState& st, const KOp& o, v4f (&s)[2][8], int t) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        if constexpr (PH == kHi) {
-            v4f d = o.bias;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.b[kk], st.qb[u][kk], d, 0, 0, 0);
-            s[u][t] = d;
-        } else {
-            s[u][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.f, st.q4[u], o.bias, kFmtFp4, kFmtFp4, 0, o.sc, 0,
-                                                                      st.q4s[u]);
-        }
-    }
-}
-
-// S^T = K . Q^T for a whole key tile (used before the pipeline starts).
-template <int PH>
-__device__ __forceinline__ void qk(const WaveState& st, const uint8_t* buf, v4f (&s)[2][8], int r, int g4) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        KOp o;
-        load_kop<PH>(o, buf, t, r, g4);
-        qk_sub<PH>(st, o, s, t);
-    }
-}
-
-__device__ __forceinline__ float max32(const v4f (&s)[8]) {
-    float a = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
-#pragma unroll
-    for (int t = 1; t < 8; ++t) a = fmaxf(fmaxf(a, s[t][0]), fmaxf(fmaxf(s[t][1], s[t][2]), s[t][3]));
-    return a;
-}
-
-__device__ __forceinline__ float cross4max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
-}
-
-// One pipelined step over the current tile (phase PC, scores s_cur, LDS
-// buffer cur) and the next tile (phase PN, LDS buffer nxt):
-//   1. row maxima of the current scores, new running max, MX group scales;
-//   2. for each key sub-tile t: the next tile's QK^T MFMAs for t next to the
-//      exponentials and conversions of the current tile's sub-tile t;
-//   3. rescale (rare), then O^T += V^T P^T and l += 1 P^T for the current tile.
-template <int PC, int PN>
-__device__ __forceinline__ void step(WaveState& st, const uint8_t* cur, const uint8_t* nxt, const v4f (&sc)[2][8],
-                                     v4f (&sn)[2][8], int e_k, int e_v, int r, int g4) {
-    const float cs = PC == kHi ? ldexpf(st.c_hi_q, e_k) : st.c_lo;
-    float mnew[2], off[2];
-    int psc[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const float gmax = max32(sc[u]);                  // this lane's 32 keys (raw scores)
-        const float tmax = cross4max(gmax) * cs;
-        mnew[u] = fmaxf(st.m[u], ceilf(tmax));
-        if constexpr (PC == kHi) {
-            off[u] = 8.0f - mnew[u];
-            psc[u] = 127;
-        } else {
-            // MX group of P = this lane's 32 keys: scale 2^F, F the smallest
-            // integer with 2^(gmax cs) <= 6 * 2^F; codes RNE(2^(x - F)).
-            const bool any = gmax > -__builtin_huge_valf();
-            const float F = any ? ceilf(gmax * cs - kLog2Six) : 0.0f;
-            off[u] = -F;
-            const int scl = any ? (int)F - (int)mnew[u] + 8 + 127 : 0;
-            psc[u] = min(254, max(0, scl));
-        }
-    }
-    // rescale when the running max grew (rare: tiles arrive best-ranked first);
-    // done before the exponentials so that nothing gets sunk below a branch
-    if (mnew[0] > st.m[0] || mnew[1] > st.m[1]) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const float f = exp2f(st.m[u] - mnew[u]);
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct) st.acc[u][ct] *= f;
-            st.lsum[u] *= f;
-        }
-    }
-    st.m[0] = mnew[0];
-    st.m[1] = mnew[1];
-    v8i pop[2];
-    KOp ko[2];
-    if constexpr (PN != kNone) load_kop<PN>(ko[0], nxt, 0, r, g4);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (PN != kNone) {
-            if (t + 1 < 8) load_kop<PN>(ko[(t + 1) & 1], nxt, t + 1, r, g4);
-            qk_sub<PN>(st, ko[t & 1], sn, t);
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            if constexpr (PC == kHi) {
-                pop[u][t] = (int)pack_fp8x4(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][t][0], cs, off[u])),
-                                            __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][t][1], cs, off[u])),
-                                            __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][t][2], cs, off[u])),
-                                            __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][t][3], cs, off[u])));
-            } else {
-                // two E2M1 codes per conversion; a dword holds sub-tiles t and t+1
-                uint32_t wv = (t & 1) ? (uint32_t)pop[u][t >> 1] : 0u;
-                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][t][0], cs, off[u]));
-                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][t][1], cs, off[u]));
-                const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][t][2], cs, off[u]));
-                const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][t][3], cs, off[u]));
-                if (t & 1) {
-                    wv = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wv, e0, e1, 1.0f, 2);
-                    wv = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wv, e2, e3, 1.0f, 3);
-                } else {
-                    wv = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wv, e0, e1, 1.0f, 0);
-                    wv = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wv, e2, e3, 1.0f, 1);
-                }
-                pop[u][t >> 1] = (int)wv;
-            }
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (PC == kLo) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            pop[u][4] = 0; pop[u][5] = 0; pop[u][6] = 0; pop[u][7] = 0;
-        }
-    }
-    // O^T += V^T . P^T and l += 1 . P^T
-    v8i ones;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) ones[q] = PC == kHi ? 0x38383838 : (q < 4 ? 0x22222222 : 0);
-    constexpr int fmt = PC == kHi ? kFmtFp8 : kFmtFp4;
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-        const int c = 16 * ct + r;
-        v8i vop;
-        int vsc;
-        if constexpr (PC == kHi) {
-            const int sw = swz_v8(c);
-            const uint4 x = *reinterpret_cast<const uint4*>(cur + kHiV + c * 128 + ((g4 ^ sw) << 4));
-            const uint4 y = *reinterpret_cast<const uint4*>(cur + kHiV + c * 128 + (((4 + g4) ^ sw) << 4));
-            vop[0] = (int)x.x; vop[1] = (int)x.y; vop[2] = (int)x.z; vop[3] = (int)x.w;
-            vop[4] = (int)y.x; vop[5] = (int)y.y; vop[6] = (int)y.z; vop[7] = (int)y.w;
-            vsc = e_v + 127;
-        } else {
-            const uint4 x = *reinterpret_cast<const uint4*>(cur + kLoV + c * 64 + ((g4 ^ swz_v4(c)) << 4));
-            vop[0] = (int)x.x; vop[1] = (int)x.y; vop[2] = (int)x.z; vop[3] = (int)x.w;
-            vop[4] = 0; vop[5] = 0; vop[6] = 0; vop[7] = 0;
-            vsc = cur[kLoS + 512 + c * 4 + g4];
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            st.acc[u][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, pop[u], st.acc[u][ct], fmt, fmt, 0, vsc, 0,
-                                                                             psc[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-        st.lsum[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pop[u], st.lsum[u], fmt, fmt, 0, 127, 0, psc[u]);
-}
-
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    const uint32_t b = __float_as_uint(f);
-    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
-
-// The key tile at position idx of the query block's list (hi blocks first).
-__device__ __forceinline__ Tile tile_at(const AttnArgs& a, int bh, int qb, int idx) {
+__device__ __forceinline__ Tile tile_at(const AttnArgs& a, const uint8_t* __restrict__ ws, const int32_t* tl, int bh,
+                                        int idx) {
     const Geo& g = a.g;
-    const uint8_t* ws = a.ws;
-    const uint64_t qtile = (uint64_t)bh * g.n_blocks + qb;
+    const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane(tl[idx]);
+    const int kb = (int)(e & 0xFFFFu);
+    const uint64_t kt = (uint64_t)bh * g.n_blocks + kb;
     Tile t;
-    int kb;
-    if (idx < g.n_hi) {
-        kb = reinterpret_cast<const int32_t*>(ws + a.L.hi)[qtile * g.n_hi + idx];
-        const uint64_t kt = (uint64_t)bh * g.n_blocks + kb;
+    if constexpr (PH == kHi) {
+        t.hi = 1;
         t.k = ws + a.L.kb + kt * (DA2_TILE * DA2_DPAD * 2);
         t.v = ws + a.L.v8t + kt * (DA2_DPAD * DA2_TILE);
         t.ks = nullptr;
         t.vs = nullptr;
-        const uint64_t plane = (uint64_t)g.bh * g.n_blocks;
-        t.e_k = (int)ws[a.L.e8 + plane + kt] - 127;
-        t.e_v = (int)ws[a.L.e8 + 2 * plane + kt] - 127;
+        t.e_k = (int)((e >> 16) & 0xFFu) - 127;
+        t.e_v = (int)(e >> 24) - 127;
     } else {
-        kb = reinterpret_cast<const int32_t*>(ws + a.L.lo)[qtile * g.n_lo + (idx - g.n_hi)];
-        const uint64_t kt = (uint64_t)bh * g.n_blocks + kb;
+        t.hi = 0;
         t.k = ws + a.L.k4 + kt * (DA2_TILE * DA2_DPAD / 2);
         t.v = ws + a.L.v4t + kt * (DA2_DPAD * DA2_TILE / 2);
         t.ks = ws + a.L.sk4 + kt * (DA2_TILE * 4);
@@ -381,17 +195,338 @@ __device__ __forceinline__ Tile tile_at(const AttnArgs& a, int bh, int qb, int i
     return t;
 }
 
-__device__ __forceinline__ void dma_tile(const AttnArgs& a, const Tile& t, int idx, uint8_t* buf, int w, int lane,
-                                         const DmaOffsets& o) {
-    if (idx < a.g.n_hi)
-        dma_tile_hi(t, buf, w, lane, o);
-    else
-        dma_tile_lo(t, buf, w, lane, o);
+// K part of a tile into a K slot, spread over the eight waves.
+template <int PH>
+__device__ __forceinline__ void dma_k(const Tile& t, uint8_t* slot, int w, int lane, const DmaOffsets& o) {
+    if constexpr (PH == kHi) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int wr = w + 8 * n;        // 32 rows of bf16 K
+            dma16(t.k + wr * 1024 + (o.k8 ^ ((wr & 4) << 4)), slot + wr * 1024);
+        }
+    } else {
+        dma16(t.k + w * 1024 + (o.k4 ^ ((w & 2) << 4)), slot + w * 1024);     // 8 rows of E2M1 K
+        if (w == 1 && lane < 32) dma16(t.ks + lane * 16, slot + kKScale);
+    }
+    if (w == 0 && lane < 32) dma16(reinterpret_cast<const uint8_t*>(t.bias) + lane * 16, slot + kKBias);
+}
+
+// V part of a tile into a V slot.
+template <int PH>
+__device__ __forceinline__ void dma_v(const Tile& t, uint8_t* slot, int w, int lane, const DmaOffsets& o) {
+    if constexpr (PH == kHi) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int wr = w + 8 * n;        // 16 rows of E4M3 V^T
+            dma16(t.v + wr * 1024 + o.v8, slot + wr * 1024);
+        }
+    } else {
+        dma16(t.v + w * 1024 + o.v4, slot + w * 1024);                        // 8 rows of E2M1 V^T
+        if (w == 3 && lane < 32) dma16(t.vs + lane * 16, slot + kVScale);
+    }
+}
+
+struct WaveState {
+    const uint8_t* q;      // LDS Q block
+    int qs0;               // first query slot of this wave
+    v4f acc[2][8];         // O^T: [u][channel tile]; lane holds channels 16ct + 4g + e of query r
+    v4f lsum[2];           // row sums (all four elements equal)
+    float m[2];            // running integer max (log2 units)
+    float c_lo;            // tau * log2(e)
+    float c_hi_q;          // tau * log2(e) * 2^e_q8
+};
+
+// A 16x16x128 MFMA operand in E2M1 occupies four registers; the builtin takes
+// eight, of which the hardware reads the first four for this format. Building
+// the vector at the call keeps only the four live values in registers.
+__device__ __forceinline__ v8i fp4_operand(v4i x) {
+    return __builtin_shufflevector(x, (v4i){0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ v4i as_v4i(const uint4& x) { return (v4i){(int)x.x, (int)x.y, (int)x.z, (int)x.w}; }
+
+// ---- Q operands of the wave's two query tiles, read from LDS ----
+// Q rows in LDS are swizzled like the K rows: bf16 16-byte chunk c of query
+// slot q sits at chunk c ^ (q & 7); E2M1 chunk c at c ^ ((q >> 1) & 3).
+struct QOps {
+    v8bf qb[2][4];         // bf16 (fp8 phase): [u][k-chunk]
+    v4i q4[2];             // E2M1 (MXFP4 phase)
+    int q4s[2];            // E8M0 scale of the lane's 32-channel group
+};
+
+template <int PH>
+__device__ __forceinline__ void load_q(const WaveState& st, QOps& qo, int r, int g4) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int qs = st.qs0 + 16 * u + r;
+        if constexpr (PH == kHi) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                qo.qb[u][kk] = __builtin_bit_cast(
+                    v8bf, *reinterpret_cast<const uint4*>(st.q + kQb + qs * 256 + (((4 * kk + g4) ^ (qs & 7)) << 4)));
+        } else {
+            const uint4 x = *reinterpret_cast<const uint4*>(st.q + kQ4 + qs * 64 + ((g4 ^ ((qs >> 1) & 3)) << 4));
+            qo.q4[u] = as_v4i(x);
+            qo.q4s[u] = st.q[kQs + qs * 4 + g4];
+        }
+    }
+}
+
+// Operands of one 16-key step t of a key tile.
+struct KHiOps {
+    v8bf k[4];
+    v4f b;                 // bias of the lane's four keys (0 or -inf)
+};
+struct KLoOps {
+    v4i k;
+    v4f b;
+    int sc;
+};
+
+__device__ __forceinline__ void load_k_hi(const uint8_t* ks, int t, int r, int g4, KHiOps& o) {
+    const int srow = slot_fp8(t, r);
+    const int sw = swz_k8(srow);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        o.k[kk] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(ks + srow * 256 + (((4 * kk + g4) ^ sw) << 4)));
+    o.b = *reinterpret_cast<const v4f*>(ks + kKBias + 4 * slot_fp8(t, 4 * g4));
+}
+
+__device__ __forceinline__ void load_k_lo(const uint8_t* ks, int t, int r, int g4, KLoOps& o) {
+    const int srow = slot_fp4(t, r);
+    const uint4 x = *reinterpret_cast<const uint4*>(ks + srow * 64 + ((g4 ^ swz_k4(srow)) << 4));
+    o.k = as_v4i(x);
+    o.sc = ks[kKScale + srow * 4 + g4];
+    o.b = *reinterpret_cast<const v4f*>(ks + kKBias + 4 * slot_fp4(t, 4 * g4));
+}
+
+// ---- S^T = K . Q^T for one key tile ----
+// The LDS reads of step t + D are issued before the MFMAs of step t (D = 1
+// for the fp8 phase, whose steps are eight MFMAs long; D = 2 for MXFP4, two
+// MFMAs per step), so the MFMA pipe does not wait for LDS latency.
+template <int PH>
+__device__ __forceinline__ void qk(const uint8_t* ks, QOps& qo, v4f (&s)[2][8], int r, int g4) {
+    if constexpr (PH == kHi) {
+        KHiOps o[2];
+        load_k_hi(ks, 0, r, g4, o[0]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if (t + 1 < 8) load_k_hi(ks, t + 1, r, g4, o[(t + 1) & 1]);
+            KHiOps& c = o[t & 1];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                v4f d = c.b;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.k[kk], qo.qb[u][kk], d, 0, 0, 0);
+                s[u][t] = d;
+            }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) keep(c.k[kk]);
+            fence();
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) keep(qo.qb[u][kk]);
+    } else {
+        constexpr int D = 2;
+        KLoOps o[D + 1];
+#pragma unroll
+        for (int t = 0; t < D; ++t) load_k_lo(ks, t, r, g4, o[t]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if (t + D < 8) load_k_lo(ks, t + D, r, g4, o[(t + D) % (D + 1)]);
+            KLoOps& c = o[t % (D + 1)];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                s[u][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(c.k), fp4_operand(qo.q4[u]), c.b, kFmtFp4,
+                                                                          kFmtFp4, 0, c.sc, 0, qo.q4s[u]);
+            keep(c.k);
+            fence();
+        }
+        keep(qo.q4[0]);
+        keep(qo.q4[1]);
+    }
+}
+
+// x *= f, computed in x's own registers. A plain multiply on a rarely taken
+// branch lets the register allocator place the product elsewhere, and the
+// merge after the branch then costs a copy of the whole accumulator on the
+// common path.
+__device__ __forceinline__ void scale_in_place(v4f& x, float f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float y = x[e];
+        asm("v_mul_f32 %0, %0, %1" : "+v"(y) : "v"(f));
+        x[e] = y;
+    }
+}
+
+__device__ __forceinline__ float max32(const v4f (&s)[8]) {
+    float a = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+#pragma unroll
+    for (int t = 1; t < 8; ++t) a = fmaxf(fmaxf(a, s[t][0]), fmaxf(fmaxf(s[t][1], s[t][2]), s[t][3]));
+    return a;
+}
+
+// Max over the four lanes l, l^16, l^32, l^48. Each permlane swap exchanges
+// two halves of a copy of v with each other, so the maximum of its two
+// results is the pairwise maximum whichever half moves where; no LDS traffic.
+__device__ __forceinline__ float cross4max(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t um = __float_as_uint(m);
+    const auto b = __builtin_amdgcn_permlane16_swap(um, um, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// ---- softmax of one tile: P operands and their E8M0 scales; rescale ----
+template <int PH>
+__device__ __forceinline__ void softmax(WaveState& st, const v4f (&s)[2][8], int e_k, v8i (&pop)[2], int (&psc)[2]) {
+    const float cs = PH == kHi ? ldexpf(st.c_hi_q, e_k) : st.c_lo;
+    float mnew[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const float gmax = max32(s[u]);                  // this lane's 32 keys (raw scores)
+        mnew[u] = fmaxf(st.m[u], ceilf(cross4max(gmax) * cs));
+        if constexpr (PH == kHi) {
+            const float off = 8.0f - mnew[u];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                pop[u][t] = (int)pack_fp8x4(__builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][0], cs, off)),
+                                            __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][1], cs, off)),
+                                            __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][2], cs, off)),
+                                            __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][3], cs, off)));
+                if ((t & 1) == 1) fence();
+            }
+            psc[u] = 127;
+        } else {
+            // MX group of P = this lane's 32 keys: scale 2^F, F the smallest
+            // integer with 2^(gmax cs) <= 6 * 2^F; codes RNE(2^(x - F)).
+            const bool any = gmax > -__builtin_huge_valf();
+            const float F = any ? ceilf(gmax * cs - kLog2Six) : 0.0f;
+            const float off = -F;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                float v[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    v[q] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][2 * d + (q >> 2)][q & 3], cs, off));
+                pop[u][d] = (int)pack_fp4x8(v);
+                fence();
+            }
+            const int sc = any ? (int)F - (int)mnew[u] + 8 + 127 : 0;
+            psc[u] = min(254, max(0, sc));
+        }
+    }
+    // rescale when the running max grew (rare: tiles arrive best-ranked first)
+    if (mnew[0] > st.m[0] || mnew[1] > st.m[1]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const float f = exp2f(st.m[u] - mnew[u]);
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) scale_in_place(st.acc[u][ct], f);
+            scale_in_place(st.lsum[u], f);
+        }
+    }
+    st.m[0] = mnew[0];
+    st.m[1] = mnew[1];
+}
+
+// ---- O^T += V^T . P^T and l += 1 . P^T ----
+// V^T operands of channel tile ct are read three tiles ahead of their MFMAs.
+template <int PH>
+struct VOps;
+template <>
+struct VOps<kHi> {
+    v8i v;                 // E4M3
+    int sc;
+};
+template <>
+struct VOps<kLo> {
+    v4i v;                 // E2M1
+    int sc;
+};
+
+template <int PH>
+__device__ __forceinline__ void load_v(const uint8_t* vs, int ct, int r, int g4, int e_v, VOps<PH>& o) {
+    const int c = 16 * ct + r;
+    if constexpr (PH == kHi) {
+        const int sw = swz_v8(c);
+        const uint4 x = *reinterpret_cast<const uint4*>(vs + c * 128 + ((g4 ^ sw) << 4));
+        const uint4 y = *reinterpret_cast<const uint4*>(vs + c * 128 + (((4 + g4) ^ sw) << 4));
+        o.v = (v8i){(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+        o.sc = e_v + 127;
+    } else {
+        o.v = as_v4i(*reinterpret_cast<const uint4*>(vs + c * 64 + ((g4 ^ swz_v4(c)) << 4)));
+        o.sc = vs[kVScale + c * 4 + g4];
+    }
+}
+
+template <int PH>
+__device__ __forceinline__ void pv(WaveState& st, const uint8_t* vs, v8i (&pop)[2], const int (&psc)[2], int e_v,
+                                   int r, int g4) {
+    constexpr int fmt = PH == kHi ? kFmtFp8 : kFmtFp4;
+    constexpr int D = 3;
+    VOps<PH> o[D + 1];
+    // B operand: P^T of the two query tiles (E2M1 uses the low four dwords)
+    v8i pb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        if constexpr (PH == kHi)
+            pb[u] = pop[u];
+        else
+            pb[u] = fp4_operand(__builtin_shufflevector(pop[u], pop[u], 0, 1, 2, 3));
+    }
+#pragma unroll
+    for (int ct = 0; ct < D; ++ct) load_v<PH>(vs, ct, r, g4, e_v, o[ct]);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+        if (ct + D < 8) load_v<PH>(vs, ct + D, r, g4, e_v, o[(ct + D) % (D + 1)]);
+        VOps<PH>& c = o[ct % (D + 1)];
+        v8i va;
+        if constexpr (PH == kHi)
+            va = c.v;
+        else
+            va = fp4_operand(c.v);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            st.acc[u][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb[u], st.acc[u][ct], fmt, fmt, 0, c.sc, 0,
+                                                                             psc[u]);
+        keep(c.v);
+        fence();
+    }
+    // all-ones A operand (E4M3 1.0 = 0x38, E2M1 1.0 = 0x2), built here so it
+    // is never kept live (or spilled) between tiles
+    int one = PH == kHi ? 0x38383838 : 0x22222222;
+    asm volatile("" : "+v"(one));          // not hoisted out of the loop
+    v8i ones;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ones[q] = (PH == kHi || q < 4) ? one : 0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+        st.lsum[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pb[u], st.lsum[u], fmt, fmt, 0, 127, 0, psc[u]);
+    keep(one);
+    if constexpr (PH == kHi) {
+        keep(pop[0]);
+        keep(pop[1]);
+    } else {
+        v4i p0 = __builtin_shufflevector(pop[0], pop[0], 0, 1, 2, 3);
+        v4i p1 = __builtin_shufflevector(pop[1], pop[1], 0, 1, 2, 3);
+        keep(p0);
+        keep(p1);
+    }
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    const uint32_t b = __float_as_uint(f);
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
 }  // namespace
 
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_t* __restrict__ ws) {
     const Geo& g = a.g;
     const int nb = g.n_blocks;
     // XCD-aware order: consecutive workgroups of one XCD take consecutive
@@ -404,131 +539,239 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const int qb = logical - bh * nb;
 
     const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0..7
+    const int team = w >> 2;
+    const int wq = w & 3;                                     // query group of this wave
     const int lane = tid & 63;
-    const int r = lane & 15;
-    const int g4 = lane >> 4;
 
-    __shared__ __align__(16) uint8_t lds[kNumBuf * kBufBytes];
+    // Separate arrays per slot: with the slot parity a compile-time constant
+    // in each phase, the compiler can see that the tile being fetched and the
+    // tiles being read never overlap, and does not wait for the fetch before
+    // reading operands.
+    __shared__ __align__(16) uint8_t kslot0[kKSlot];
+    __shared__ __align__(16) uint8_t kslot1[kKSlot];
+    __shared__ __align__(16) uint8_t vslot0[kVSlot];
+    __shared__ __align__(16) uint8_t vslot1[kVSlot];
+    __shared__ __align__(16) uint8_t qlds[kQBytes];
+    __shared__ __align__(16) int32_t tlist[kListBytes / 4];
 
-    const uint8_t* ws = a.ws;
     const uint64_t qtile = (uint64_t)bh * nb + qb;
     const int n_tiles = g.n_hi + g.n_lo;
 
-    const DmaOffsets doff = dma_offsets(lane);
-    // start the first two tiles' DMA before touching Q
-    const Tile t0 = tile_at(a, bh, qb, 0);
-    dma_tile(a, t0, 0, lds, w, lane, doff);
-    Tile t1 = t0;
-    if (n_tiles > 1) {
-        t1 = tile_at(a, bh, qb, 1);
-        dma_tile(a, t1, 1, lds + kBufBytes, w, lane, doff);
+    // this query block's tile list, packed with the fp8 exponents, into LDS
+    int32_t* tl = tlist;
+    {
+        const uint64_t plane = (uint64_t)g.bh * nb;
+        const int32_t* hl = reinterpret_cast<const int32_t*>(ws + a.L.hi) + qtile * g.n_hi;
+        const int32_t* ll = reinterpret_cast<const int32_t*>(ws + a.L.lo) + qtile * g.n_lo;
+        for (int i = tid; i < n_tiles; i += kThreads) {
+            uint32_t e;
+            if (i < g.n_hi) {
+                const int kb = hl[i];
+                const uint64_t kt = (uint64_t)bh * nb + kb;
+                e = (uint32_t)kb | ((uint32_t)ws[a.L.e8 + plane + kt] << 16) | ((uint32_t)ws[a.L.e8 + 2 * plane + kt] << 24);
+            } else {
+                e = (uint32_t)ll[i - g.n_hi];
+            }
+            tl[i] = (int32_t)e;
+        }
+    }
+    __syncthreads();
+
+    // the query block's Q operands (swizzled rows)
+    {
+        const uint8_t* qb_src = ws + a.L.qb + qtile * (DA2_TILE * DA2_DPAD * 2);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {                 // 32 KiB: 32 rows of 1 KiB
+            const int wr = w + 8 * n;
+            const int p = wr * 64 + lane;
+            const int q = p >> 4, pc = p & 15;
+            dma16(qb_src + (q * 16 + (pc ^ (q & 7))) * 16, qlds + kQb + wr * 1024);
+        }
+        const uint8_t* q4_src = ws + a.L.q4 + qtile * (DA2_TILE * DA2_DPAD / 2);
+        {                                             // 8 KiB: 8 rows
+            const int p = w * 64 + lane;
+            const int q = p >> 2, pc = p & 3;
+            dma16(q4_src + (q * 4 + (pc ^ ((q >> 1) & 3))) * 16, qlds + kQ4 + w * 1024);
+        }
+        if (w == 2 && lane < 32)
+            dma16(ws + a.L.sq4 + qtile * (DA2_TILE * DA2_DPAD / 32) + lane * 16, qlds + kQs);
     }
 
     WaveState st;
+    st.q = qlds;
+    st.qs0 = 32 * wq;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int qs = 32 * w + 16 * u + r;
-        const uint8_t* rowb = ws + a.L.qb + (qtile * (DA2_TILE * DA2_DPAD) + qs * DA2_DPAD) * 2;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            st.qb[u][kk] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(rowb + 64 * kk + 16 * g4));
-        const uint8_t* row4 = ws + a.L.q4 + qtile * (DA2_TILE * DA2_DPAD / 2) + qs * (DA2_DPAD / 2);
-        const uint4 x4 = *reinterpret_cast<const uint4*>(row4 + 16 * g4);
-        st.q4[u][0] = (int)x4.x; st.q4[u][1] = (int)x4.y; st.q4[u][2] = (int)x4.z; st.q4[u][3] = (int)x4.w;
-        st.q4[u][4] = 0; st.q4[u][5] = 0; st.q4[u][6] = 0; st.q4[u][7] = 0;
-        st.q4s[u] = (int)ws[a.L.sq4 + qtile * (DA2_TILE * DA2_DPAD / 32) + qs * (DA2_DPAD / 32) + g4];
         st.m[u] = -__builtin_huge_valf();
         st.lsum[u] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) st.acc[u][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
-    st.c_lo = (float)g.tau * kLog2E;
-    st.c_hi_q = ldexpf(st.c_lo, (int)ws[a.L.e8 + qtile] - 127);
-
-    v4f sA[2][8], sB[2][8];
-    __builtin_amdgcn_s_waitcnt(0);     // tiles 0 and 1 and the Q operands
+    st.c_lo = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, (float)g.tau * kLog2E)));
+    {
+        // uniform: kept in a scalar register
+        const float c = ldexpf(st.c_lo, __builtin_amdgcn_readfirstlane((int)ws[a.L.e8 + qtile]) - 127);
+        st.c_hi_q = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c)));
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (g.n_hi > 0)
-        qk<kHi>(st, lds, sA, r, g4);
-    else
-        qk<kLo>(st, lds, sA, r, g4);
 
-    // Tile idx lives in buffer idx % 3; its scores are in sA when it is the
-    // current tile. Each step first issues the DMA of tile idx + 2 into the
-    // buffer of tile idx - 1, whose readers all passed the previous barrier.
-    Tile cur = t0, nxt = t1;
-    int idx = 0;
-    auto issue_next = [&]() {
-        Tile t2 = nxt;
-        if (idx + 2 < n_tiles) {
-            t2 = tile_at(a, bh, qb, idx + 2);
-            dma_tile(a, t2, idx + 2, lds + ((idx + 2) % 3) * kBufBytes, w, lane, doff);
-        }
-        return t2;
-    };
-    auto finish = [&](const Tile& t2) {
-        cur = nxt;
-        nxt = t2;
-        ++idx;
+    v4f s[2][8];
+    v8i pop[2];
+    int psc[2];
+
+    // The tile list is run as two sections, its hi tiles and then its lo
+    // tiles, each through the same software pipeline; inside a section every
+    // step has one precision, so the loop bodies carry no precision branches.
+    //
+    // Within a section of n tiles, phase p (0 <= p < n + 2): team p%2 runs
+    // PV(p-2) and QK^T(p); the other team runs the softmax of tile p-1. So
+    // each team owns every other tile: its QK^T in phase j, softmax in phase
+    // j+1, PV in phase j+2. K(p+1) and V(p-1) are fetched during phase p into
+    // the slots of K(p-1) and V(p-3), whose readers finished in phase p-1;
+    // each is waited for at the end of phase p and first read in phase p+1.
+    // Each team runs its own copy of the loop, two phases per trip, so the
+    // lifetimes of S and P are static and the slot parity of every access is
+    // a compile-time constant.
+    auto sync = [&]() __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
-    // fp8 phase, pipelined while the next tile is fp8 too
-    for (; idx + 1 < g.n_hi; ) {
-        const Tile t2 = issue_next();
-        step<kHi, kHi>(st, lds + (idx % 3) * kBufBytes, lds + ((idx + 1) % 3) * kBufBytes, sA, sB, cur.e_k, cur.e_v, r, g4);
+    auto section = [&](auto ph, int base, int n) __attribute__((always_inline)) {
+        constexpr int PH = decltype(ph)::value;
+        auto tile = [&](int j) __attribute__((always_inline)) { return tile_at<PH>(a, ws, tl, bh, base + j); };
+        auto fetch = [&](auto par, int p) __attribute__((always_inline)) {
+            constexpr int PAR = decltype(par)::value;
+            // lane offsets recomputed here (a handful of ALU ops) rather than
+            // kept live across the loop, where they would be spilled
+            const int ln = fresh_lane();
+            const DmaOffsets o = dma_offsets(ln);
+            // K(p+1) and V(p-1) both go to the slots of parity PAR ^ 1
+            if (p + 1 < n) dma_k<PH>(tile(p + 1), PAR ? kslot0 : kslot1, w, ln, o);
+            if (p >= 1 && p - 1 < n) dma_v<PH>(tile(p - 1), PAR ? vslot0 : vslot1, w, ln, o);
+        };
+        auto mma_phase = [&](auto par, int p) __attribute__((always_inline)) {
+            constexpr int PAR = decltype(par)::value;
+            // the lane coordinates are recomputed here, not kept live
+            const int ln = fresh_lane();
+            const int r = ln & 15, g4 = ln >> 4;
+            // Q operands for this phase's QK^T are read first, under the PV
+            QOps qo;
+            if (p < n) load_q<PH>(st, qo, r, g4);
+            if (p >= 2) pv<PH>(st, PAR ? vslot1 : vslot0, pop, psc, PH == kHi ? tile(p - 2).e_v : 0, r, g4);
+            if (p < n) {
+                qk<PH>(PAR ? kslot1 : kslot0, qo, s, r, g4);
+            } else {
+                // defined on every path, so the previous scores are dead here
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+                for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) sA[u][t] = sB[u][t];
-        finish(t2);
-    }
-    if (g.n_hi > 0) {
-        // last fp8 tile, then the first MXFP4 tile's QK^T on its own
-        const Tile t2 = issue_next();
-        step<kHi, kNone>(st, lds + (idx % 3) * kBufBytes, lds, sA, sB, cur.e_k, cur.e_v, r, g4);
-        finish(t2);
-        if (idx < n_tiles) qk<kLo>(st, lds + (idx % 3) * kBufBytes, sA, r, g4);
-    }
-    // MXFP4 phase
-    for (; idx + 1 < n_tiles; ) {
-        const Tile t2 = issue_next();
-        step<kLo, kLo>(st, lds + (idx % 3) * kBufBytes, lds + ((idx + 1) % 3) * kBufBytes, sA, sB, 0, 0, r, g4);
+                    for (int t = 0; t < 8; ++t) s[u][t] = (v4f){0.f, 0.f, 0.f, 0.f};
+            }
+        };
+        auto softmax_phase = [&](int p) __attribute__((always_inline)) {
+            if (p >= 1 && p - 1 < n) {
+                softmax<PH>(st, s, PH == kHi ? tile(p - 1).e_k : 0, pop, psc);
+            } else {
+                // defined on every path, so the previous P is dead here
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+                for (int u = 0; u < 2; ++u) {
+                    psc[u] = 127;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) sA[u][t] = sB[u][t];
-        finish(t2);
-    }
-    if (idx < n_tiles) {
-        step<kLo, kNone>(st, lds + (idx % 3) * kBufBytes, lds, sA, sB, 0, 0, r, g4);
-    }
+                    for (int q = 0; q < 8; ++q) pop[u][q] = 0;
+                }
+            }
+        };
+        using Even = std::integral_constant<int, 0>;
+        using Odd = std::integral_constant<int, 1>;
+        // the section's first K tile
+        {
+            const int ln = fresh_lane();
+            dma_k<PH>(tile(0), kslot0, w, ln, dma_offsets(ln));
+            sync();
+        }
+        const int n_phases = n + 2;
+        if (team == 0) {
+            for (int p = 0; p < n_phases; p += 2) {
+                fetch(Even{}, p);
+                mma_phase(Even{}, p);
+                sync();
+                if (p + 1 < n_phases) {
+                    fetch(Odd{}, p + 1);
+                    softmax_phase(p + 1);
+                    sync();
+                }
+            }
+        } else {
+            for (int p = 0; p < n_phases; p += 2) {
+                fetch(Even{}, p);
+                softmax_phase(p);
+                sync();
+                if (p + 1 < n_phases) {
+                    fetch(Odd{}, p + 1);
+                    mma_phase(Odd{}, p + 1);
+                    sync();
+                }
+            }
+        }
+    };
+    if (g.n_hi > 0) section(std::integral_constant<int, kHi>{}, 0, g.n_hi);
+    if (g.n_lo > 0) section(std::integral_constant<int, kLo>{}, g.n_hi, g.n_lo);
 
-    // ================= epilogue: O = acc / l, back to raster order =================
+    const int r = lane & 15, g4 = lane >> 4;
+    // ---- merge the two teams: team 1 hands (m, l, acc) to team 0 through LDS ----
+    // 66 floats per lane (acc and l of both query tiles): 16896 B per wave,
+    // two waves per K slot
+    float* xch = reinterpret_cast<float*>(wq < 2 ? kslot0 : kslot1) + (size_t)(wq & 1) * (66 * 64);
+    if (team == 1) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xch[((u * 8 + ct) * 4 + e) * 64 + lane] = st.acc[u][ct][e];
+            xch[(64 + u) * 64 + lane] = st.lsum[u][0];
+        }
+    }
+    float* xm = reinterpret_cast<float*>(vslot0) + wq * 128;     // m: 2 x 64 floats per wave
+    if (team == 1) {
+        xm[lane] = st.m[0];
+        xm[64 + lane] = st.m[1];
+    }
+    __syncthreads();
+    if (team == 1) return;
+
     const BlockPos qp = block_pos(g, qb);
     const int b = bh / g.heads;
     const int h = bh - b * g.heads;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int qs = 32 * w + 16 * u + r;
+        const float m1 = xm[u * 64 + lane];
+        const float l1 = xch[(64 + u) * 64 + lane];
+        const float mm = fmaxf(st.m[u], m1);
+        const float f0 = st.m[u] > -__builtin_huge_valf() ? exp2f(st.m[u] - mm) : 0.0f;
+        const float f1 = m1 > -__builtin_huge_valf() ? exp2f(m1 - mm) : 0.0f;
+        const float inv = 1.0f / (st.lsum[u][0] * f0 + l1 * f1);
+        const int qs = 32 * wq + 16 * u + r;
         const int64_t n = slot_raster(g, qp, qs);
         if (n < 0) continue;
-        const float inv = 1.0f / st.lsum[u][0];
         const int64_t rowoff = (int64_t)b * g.stride_b + (int64_t)h * g.stride_h + n * g.stride_n;
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
             const int c = 16 * ct + 4 * g4;
             if (c >= g.head_dim) continue;
-            const float o0 = st.acc[u][ct][0] * inv, o1 = st.acc[u][ct][1] * inv;
-            const float o2 = st.acc[u][ct][2] * inv, o3 = st.acc[u][ct][3] * inv;
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = (st.acc[u][ct][e] * f0 + xch[((u * 8 + ct) * 4 + e) * 64 + lane] * f1) * inv;
             if (a.out_fp32) {
-                *reinterpret_cast<float4*>(static_cast<float*>(a.out) + rowoff + c) = make_float4(o0, o1, o2, o3);
+                *reinterpret_cast<float4*>(static_cast<float*>(a.out) + rowoff + c) = make_float4(o[0], o[1], o[2], o[3]);
             } else {
-                uint2 p;
-                p.x = f32_to_bf16_rne(o0) | (f32_to_bf16_rne(o1) << 16);
-                p.y = f32_to_bf16_rne(o2) | (f32_to_bf16_rne(o3) << 16);
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + rowoff + c) = p;
+                uint2 pk;
+                pk.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
+                pk.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + rowoff + c) = pk;
             }
         }
     }
@@ -543,7 +786,7 @@ hipError_t launch_attention(const Geo& g, const Layout& L, const void* ws, void*
     a.out = out;
     a.out_fp32 = out_fp32;
     const int total = g.bh * g.n_blocks;
-    return launch_kernel(attn_kernel, dim3(total), dim3(kThreads), 0, stream, a);
+    return launch_kernel(attn_kernel, dim3(total), dim3(kThreads), 0, stream, a, a.ws);
 }
 
 }  // namespace da2
