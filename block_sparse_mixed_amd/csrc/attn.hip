@@ -232,6 +232,7 @@ struct WaveState {
     v4f acc[2][8];         // O^T: [u][channel tile]; lane holds channels 16ct + 4g + e of query r
     v4f lsum[2];           // row sums (all four elements equal)
     float m[2];            // running integer max (log2 units)
+    float mref[2];         // acc and lsum hold values relative to 2^mref
     float c_lo;            // tau * log2(e)
     float c_hi_q;          // tau * log2(e) * 2^e_q8
 };
@@ -381,15 +382,38 @@ __device__ __forceinline__ float cross4max(float v) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// ---- softmax of one tile: P operands and their E8M0 scales; rescale ----
+// ---- softmax of one tile: P operands and their E8M0 scales ----
+// The P codes of a tile are taken relative to the running integer max m (so
+// they are the codes the oracle takes relative to the final max, shifted by
+// a power of two). The accumulator and row sum are kept relative to a
+// reference 2^mref instead, and the factor 2^(m - mref) rides in the P scale
+// operand of the PV and row-sum MFMAs: a growing maximum costs no pass over
+// the accumulator. Only when m runs more than kMaxLead above mref (or at the
+// first tile, mref = -inf) is the accumulator rescaled, by an exact power of
+// two, and mref moved to m.
+constexpr float kMaxLead = 64.0f;
+
 template <int PH>
 __device__ __forceinline__ void softmax(WaveState& st, const v4f (&s)[2][8], int e_k, v8i (&pop)[2], int (&psc)[2]) {
     const float cs = PH == kHi ? ldexpf(st.c_hi_q, e_k) : st.c_lo;
-    float mnew[2];
+    float gmax[2], mnew[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const float gmax = max32(s[u]);                  // this lane's 32 keys (raw scores)
-        mnew[u] = fmaxf(st.m[u], ceilf(cross4max(gmax) * cs));
+        gmax[u] = max32(s[u]);                           // this lane's 32 keys (raw scores)
+        mnew[u] = fmaxf(st.m[u], ceilf(cross4max(gmax[u]) * cs));
+    }
+    if (!(st.mref[0] >= mnew[0] - kMaxLead) || !(st.mref[1] >= mnew[1] - kMaxLead)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const float f = exp2f(st.mref[u] - mnew[u]);  // 0 while mref = -inf
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) scale_in_place(st.acc[u][ct], f);
+            scale_in_place(st.lsum[u], f);
+            st.mref[u] = mnew[u];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
         if constexpr (PH == kHi) {
             const float off = 8.0f - mnew[u];
 #pragma unroll
@@ -400,12 +424,12 @@ __device__ __forceinline__ void softmax(WaveState& st, const v4f (&s)[2][8], int
                                             __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][3], cs, off)));
                 if ((t & 1) == 1) fence();
             }
-            psc[u] = 127;
+            psc[u] = 127 + (int)(mnew[u] - st.mref[u]);      // 127 .. 127 + kMaxLead
         } else {
             // MX group of P = this lane's 32 keys: scale 2^F, F the smallest
             // integer with 2^(gmax cs) <= 6 * 2^F; codes RNE(2^(x - F)).
-            const bool any = gmax > -__builtin_huge_valf();
-            const float F = any ? ceilf(gmax * cs - kLog2Six) : 0.0f;
+            const bool any = gmax[u] > -__builtin_huge_valf();
+            const float F = any ? ceilf(gmax[u] * cs - kLog2Six) : 0.0f;
             const float off = -F;
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
@@ -416,18 +440,8 @@ __device__ __forceinline__ void softmax(WaveState& st, const v4f (&s)[2][8], int
                 pop[u][d] = (int)pack_fp4x8(v);
                 fence();
             }
-            const int sc = any ? (int)F - (int)mnew[u] + 8 + 127 : 0;
+            const int sc = any ? (int)(F - st.mref[u]) + 8 + 127 : 0;
             psc[u] = min(254, max(0, sc));
-        }
-    }
-    // rescale when the running max grew (rare: tiles arrive best-ranked first)
-    if (mnew[0] > st.m[0] || mnew[1] > st.m[1]) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const float f = exp2f(st.m[u] - mnew[u]);
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct) scale_in_place(st.acc[u][ct], f);
-            scale_in_place(st.lsum[u], f);
         }
     }
     st.m[0] = mnew[0];
@@ -604,6 +618,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         st.m[u] = -__builtin_huge_valf();
+        st.mref[u] = -__builtin_huge_valf();
         st.lsum[u] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) st.acc[u][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -736,8 +751,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
     }
     float* xm = reinterpret_cast<float*>(vslot0) + wq * 128;     // m: 2 x 64 floats per wave
     if (team == 1) {
-        xm[lane] = st.m[0];
-        xm[64 + lane] = st.m[1];
+        xm[lane] = st.mref[0];
+        xm[64 + lane] = st.mref[1];
     }
     __syncthreads();
     if (team == 1) return;
@@ -749,8 +764,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
     for (int u = 0; u < 2; ++u) {
         const float m1 = xm[u * 64 + lane];
         const float l1 = xch[(64 + u) * 64 + lane];
-        const float mm = fmaxf(st.m[u], m1);
-        const float f0 = st.m[u] > -__builtin_huge_valf() ? exp2f(st.m[u] - mm) : 0.0f;
+        const float mm = fmaxf(st.mref[u], m1);
+        const float f0 = st.mref[u] > -__builtin_huge_valf() ? exp2f(st.mref[u] - mm) : 0.0f;
         const float f1 = m1 > -__builtin_huge_valf() ? exp2f(m1 - mm) : 0.0f;
         const float inv = 1.0f / (st.lsum[u][0] * f0 + l1 * f1);
         const int qs = 32 * wq + 16 * u + r;

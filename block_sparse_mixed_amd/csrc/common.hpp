@@ -84,7 +84,10 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __ui
 
 // Four values -> four E4M3 codes (round to nearest even), packed low byte first.
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    // the first conversion writes the low half and keeps the high half of
+    // its "old" operand, which the second conversion overwrites: any old
+    // value will do, and reusing a's register saves a move
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
 }
@@ -101,7 +104,8 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t codes) {
 // Eight values -> eight E2M1 codes (round to nearest even, saturating at 6),
 // packed low nibble first.
 __device__ __forceinline__ uint32_t pack_fp4x8(const float* v) {
-    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], 1.0f, 0);
+    // every byte is written below, so the "old" operand is irrelevant
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(__float_as_uint(v[0]), v[0], v[1], 1.0f, 0);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
