@@ -20,7 +20,9 @@
 //   a SIMD are therefore always in opposite halves of their work: one keeps
 //   the MFMA pipe busy while the other exponentiates.
 //     S^T = K . Q^T        fp8 tiles: V_MFMA_F32_16X16X32_BF16 on the E4M3
-//                          values decoded to bf16 (exact);
+//                          values widened to bf16 (exact): Q once by the
+//                          preparation kernel, K in registers from the E4M3
+//                          codes in LDS;
 //                          MXFP4 tiles: V_MFMA_SCALE_F32_16X16X128_F8F6F4
 //     softmax (base 2, integer running max per team, lane-local rescale)
 //     O^T += V^T . P^T     scaled f8f6f4 MFMAs (E4M3 or E2M1 operands), plus
@@ -71,6 +73,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 struct AttnArgs {
     Geo g;
@@ -83,16 +86,19 @@ struct AttnArgs {
 namespace {
 
 constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 constexpr int kFmtFp8 = 0;
 constexpr int kFmtFp4 = 4;
 constexpr float kLog2E = 1.4426950408889634f;
 constexpr float kLog2Six = 2.5849625007211562f;
 constexpr int kHi = 0, kLo = 1;
 
-// LDS: K slots [K data 32 KiB | bias f32[128] | E8M0 K scales [128][4]] and
-// V slots [V^T data 16 KiB | E8M0 V scales [128][4]], two of each, and Q.
-// fp8 tiles: K data = bf16 [128 slots][256 B], V data = E4M3 [128 ch][128 B];
+// LDS: K slots [K data | bias f32[128] | E8M0 K scales [128][4]] and V slots
+// [V^T data 16 KiB | E8M0 V scales [128][4]], two of each, and Q.
+// fp8 tiles: K data = E4M3 [128 slots][128 B], V data = E4M3 [128 ch][128 B];
 // MXFP4 tiles: K data = E2M1 [128 slots][64 B], V data = E2M1 [128 ch][64 B].
+// A K slot is sized for the exchange area of the final team merge (two waves'
+// accumulators), which it doubles as; the tiles use at most 16 KiB of it.
 constexpr int kKBias = 32768, kKScale = 33280, kKSlot = 33792;
 constexpr int kVScale = 16384, kVSlot = 16896;
 constexpr int kSlots = 2;
@@ -103,7 +109,7 @@ static_assert(2 * 66 * 64 * 4 <= kKSlot, "team merge area: two waves per K slot"
 
 // LDS swizzles (16-byte chunk index XOR a row function) so that the eight
 // lanes served together by a 128-bit LDS read hit distinct banks.
-__device__ __forceinline__ int swz_k8(int s) { return (s & 3) | ((s >> 2) & 4); }
+__device__ __forceinline__ int swz_k8f(int s) { return ((s >> 1) & 1) | (((s >> 4) & 3) << 1); }
 __device__ __forceinline__ int swz_v8(int c) { return c & 7; }
 __device__ __forceinline__ int swz_k4(int s) { return ((s >> 1) & 1) | ((s >> 4) & 2); }
 __device__ __forceinline__ int swz_v4(int c) { return (c >> 1) & 3; }
@@ -141,15 +147,17 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint8_t* ldst) {
 // Per-lane gather offsets of a 1 KiB DMA row that apply the LDS swizzle; for
 // every row they reduce to a per-lane constant, XORed with a row-uniform bit.
 struct DmaOffsets {
-    uint32_t k8, v8, k4, v4;
+    uint32_t v8, k4, v4, k8f;
 };
 
 __device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
     DmaOffsets o;
-    o.k8 = ((lane >> 4) << 8) + (((lane & 15) ^ ((lane >> 4) & 3)) << 4);
     o.v8 = ((lane >> 3) << 7) + (((lane & 7) ^ (lane >> 3)) << 4);
     o.k4 = ((lane >> 2) << 6) + (((lane & 3) ^ ((lane >> 3) & 1)) << 4);
     o.v4 = ((lane >> 2) << 6) + (((lane & 3) ^ ((lane >> 3) & 3)) << 4);
+    // E4M3 K rows (128 B): chunk c of row s sits at c ^ swz_k8f(s); a DMA of
+    // rows 8i .. 8i+7 gathers with this offset XOR (((i >> 1) & 3) << 5)
+    o.k8f = ((lane >> 3) << 7) + (((lane & 7) ^ ((lane >> 4) & 1)) << 4);
     return o;
 }
 
@@ -166,17 +174,18 @@ struct Tile {
 // The key tile at position idx of the query block's list (hi blocks first),
 // from the packed copy of the list in LDS: block index in bits 0-15, biased
 // K and V fp8 exponents in bits 16-23 and 24-31.
+// The packed entry is made wave-uniform (a scalar register) so that all the
+// tile's address arithmetic is scalar.
 template <int PH>
-__device__ __forceinline__ Tile tile_at(const AttnArgs& a, const uint8_t* __restrict__ ws, const int32_t* tl, int bh,
-                                        int idx) {
+__device__ __forceinline__ Tile tile_from(const AttnArgs& a, const uint8_t* __restrict__ ws, int bh, int32_t entry) {
     const Geo& g = a.g;
-    const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane(tl[idx]);
+    const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane(entry);
     const int kb = (int)(e & 0xFFFFu);
     const uint64_t kt = (uint64_t)bh * g.n_blocks + kb;
     Tile t;
     if constexpr (PH == kHi) {
         t.hi = 1;
-        t.k = ws + a.L.kb + kt * (DA2_TILE * DA2_DPAD * 2);
+        t.k = ws + a.L.k8 + kt * (DA2_TILE * DA2_DPAD);
         t.v = ws + a.L.v8t + kt * (DA2_DPAD * DA2_TILE);
         t.ks = nullptr;
         t.vs = nullptr;
@@ -195,17 +204,27 @@ __device__ __forceinline__ Tile tile_at(const AttnArgs& a, const uint8_t* __rest
     return t;
 }
 
+template <int PH>
+__device__ __forceinline__ Tile tile_at(const AttnArgs& a, const uint8_t* __restrict__ ws, const int32_t* tl, int bh,
+                                        int idx) {
+    return tile_from<PH>(a, ws, bh, tl[idx]);
+}
+
 // K part of a tile into a K slot, spread over the eight waves.
 template <int PH>
 __device__ __forceinline__ void dma_k(const Tile& t, uint8_t* slot, int w, int lane, const DmaOffsets& o) {
     if constexpr (PH == kHi) {
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int wr = w + 8 * n;        // 32 rows of bf16 K
-            dma16(t.k + wr * 1024 + (o.k8 ^ ((wr & 4) << 4)), slot + wr * 1024);
+        for (int n = 0; n < 16 / kWaves; ++n) {
+            const int wr = w + kWaves * n;   // 16 KiB of E4M3 K: 8 key rows per wave row
+            dma16(t.k + wr * 1024 + (o.k8f ^ (((wr >> 1) & 3) << 5)), slot + wr * 1024);
         }
     } else {
-        dma16(t.k + w * 1024 + (o.k4 ^ ((w & 2) << 4)), slot + w * 1024);     // 8 rows of E2M1 K
+#pragma unroll
+        for (int n = 0; n < 8 / kWaves; ++n) {
+            const int wr = w + kWaves * n;   // 8 KiB of E2M1 K
+            dma16(t.k + wr * 1024 + (o.k4 ^ ((wr & 2) << 4)), slot + wr * 1024);
+        }
         if (w == 1 && lane < 32) dma16(t.ks + lane * 16, slot + kKScale);
     }
     if (w == 0 && lane < 32) dma16(reinterpret_cast<const uint8_t*>(t.bias) + lane * 16, slot + kKBias);
@@ -216,12 +235,16 @@ template <int PH>
 __device__ __forceinline__ void dma_v(const Tile& t, uint8_t* slot, int w, int lane, const DmaOffsets& o) {
     if constexpr (PH == kHi) {
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const int wr = w + 8 * n;        // 16 rows of E4M3 V^T
+        for (int n = 0; n < 16 / kWaves; ++n) {
+            const int wr = w + kWaves * n;   // 16 KiB of E4M3 V^T
             dma16(t.v + wr * 1024 + o.v8, slot + wr * 1024);
         }
     } else {
-        dma16(t.v + w * 1024 + o.v4, slot + w * 1024);                        // 8 rows of E2M1 V^T
+#pragma unroll
+        for (int n = 0; n < 8 / kWaves; ++n) {
+            const int wr = w + kWaves * n;   // 8 KiB of E2M1 V^T
+            dma16(t.v + wr * 1024 + o.v4, slot + wr * 1024);
+        }
         if (w == 3 && lane < 32) dma16(t.vs + lane * 16, slot + kVScale);
     }
 }
@@ -264,7 +287,7 @@ __device__ __forceinline__ void load_q(const WaveState& st, QOps& qo, int r, int
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
                 qo.qb[u][kk] = __builtin_bit_cast(
-                    v8bf, *reinterpret_cast<const uint4*>(st.q + kQb + qs * 256 + (((4 * kk + g4) ^ (qs & 7)) << 4)));
+                    v8bf, *reinterpret_cast<const uint4*>(st.q + kQb + qs * 256 + (((4 * g4 + kk) ^ (qs & 7)) << 4)));
         } else {
             const uint4 x = *reinterpret_cast<const uint4*>(st.q + kQ4 + qs * 64 + ((g4 ^ ((qs >> 1) & 3)) << 4));
             qo.q4[u] = as_v4i(x);
@@ -275,7 +298,7 @@ __device__ __forceinline__ void load_q(const WaveState& st, QOps& qo, int r, int
 
 // Operands of one 16-key step t of a key tile.
 struct KHiOps {
-    v8bf k[4];
+    uint4 k[2];            // 32 E4M3 codes: channels 32 g4 .. 32 g4 + 31
     v4f b;                 // bias of the lane's four keys (0 or -inf)
 };
 struct KLoOps {
@@ -284,13 +307,25 @@ struct KLoOps {
     int sc;
 };
 
+// The fp8 tiles keep K as E4M3 codes in LDS (half the bytes of bf16) and
+// widen them to bf16 in registers, exactly, just before the MFMAs. Lane
+// (r, g4) feeds channels 32 g4 + 8 kk .. + 7 as k-chunk kk; Q uses the same
+// assignment, which is all a bf16 MFMA requires of its operands.
 __device__ __forceinline__ void load_k_hi(const uint8_t* ks, int t, int r, int g4, KHiOps& o) {
     const int srow = slot_fp8(t, r);
-    const int sw = swz_k8(srow);
+    const int sw = swz_k8f(srow);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-        o.k[kk] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(ks + srow * 256 + (((4 * kk + g4) ^ sw) << 4)));
+    for (int h = 0; h < 2; ++h)
+        o.k[h] = *reinterpret_cast<const uint4*>(ks + srow * 128 + (((2 * g4 + h) ^ sw) << 4));
     o.b = *reinterpret_cast<const v4f*>(ks + kKBias + 4 * slot_fp8(t, 4 * g4));
+}
+
+__device__ __forceinline__ v8bf widen_e4m3(uint32_t lo, uint32_t hi) {
+    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, false);
+    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, true);
+    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, false);
+    const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, true);
+    return (v8bf){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 __device__ __forceinline__ void load_k_lo(const uint8_t* ks, int t, int r, int g4, KLoOps& o) {
@@ -314,15 +349,21 @@ __device__ __forceinline__ void qk(const uint8_t* ks, QOps& qo, v4f (&s)[2][8], 
         for (int t = 0; t < 8; ++t) {
             if (t + 1 < 8) load_k_hi(ks, t + 1, r, g4, o[(t + 1) & 1]);
             KHiOps& c = o[t & 1];
+            v8bf kb[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const uint4& x = c.k[kk >> 1];
+                kb[kk] = (kk & 1) ? widen_e4m3(x.z, x.w) : widen_e4m3(x.x, x.y);
+            }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 v4f d = c.b;
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.k[kk], qo.qb[u][kk], d, 0, 0, 0);
+                for (int kk = 0; kk < 4; ++kk) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qo.qb[u][kk], d, 0, 0, 0);
                 s[u][t] = d;
             }
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) keep(c.k[kk]);
+            for (int kk = 0; kk < 4; ++kk) keep(kb[kk]);
             fence();
         }
 #pragma unroll
@@ -596,17 +637,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
     {
         const uint8_t* qb_src = ws + a.L.qb + qtile * (DA2_TILE * DA2_DPAD * 2);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {                 // 32 KiB: 32 rows of 1 KiB
-            const int wr = w + 8 * n;
+        for (int n = 0; n < 32 / kWaves; ++n) {       // 32 KiB: 32 rows of 1 KiB
+            const int wr = w + kWaves * n;
             const int p = wr * 64 + lane;
             const int q = p >> 4, pc = p & 15;
             dma16(qb_src + (q * 16 + (pc ^ (q & 7))) * 16, qlds + kQb + wr * 1024);
         }
         const uint8_t* q4_src = ws + a.L.q4 + qtile * (DA2_TILE * DA2_DPAD / 2);
-        {                                             // 8 KiB: 8 rows
-            const int p = w * 64 + lane;
+#pragma unroll
+        for (int n = 0; n < 8 / kWaves; ++n) {      // 8 KiB: 8 rows
+            const int wr = w + kWaves * n;
+            const int p = wr * 64 + lane;
             const int q = p >> 2, pc = p & 3;
-            dma16(q4_src + (q * 4 + (pc ^ ((q >> 1) & 3))) * 16, qlds + kQ4 + w * 1024);
+            dma16(q4_src + (q * 4 + (pc ^ ((q >> 1) & 3))) * 16, qlds + kQ4 + wr * 1024);
         }
         if (w == 2 && lane < 32)
             dma16(ws + a.L.sq4 + qtile * (DA2_TILE * DA2_DPAD / 32) + lane * 16, qlds + kQs);
@@ -662,9 +705,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
             // kept live across the loop, where they would be spilled
             const int ln = fresh_lane();
             const DmaOffsets o = dma_offsets(ln);
+            // Both list entries are read before any DMA is issued (one LDS
+            // round trip); indices wrap inside the list array, and an entry
+            // outside the section is never used.
+            const int32_t ek = tl[(base + p + 1) & (DA2_MAX_BLOCKS - 1)];
+            const int32_t ev = tl[(base + p - 1) & (DA2_MAX_BLOCKS - 1)];
             // K(p+1) and V(p-1) both go to the slots of parity PAR ^ 1
-            if (p + 1 < n) dma_k<PH>(tile(p + 1), PAR ? kslot0 : kslot1, w, ln, o);
-            if (p >= 1 && p - 1 < n) dma_v<PH>(tile(p - 1), PAR ? vslot0 : vslot1, w, ln, o);
+            if (p + 1 < n) dma_k<PH>(tile_from<PH>(a, ws, bh, ek), PAR ? kslot0 : kslot1, w, ln, o);
+            if (p >= 1 && p - 1 < n) dma_v<PH>(tile_from<PH>(a, ws, bh, ev), PAR ? vslot0 : vslot1, w, ln, o);
         };
         auto mma_phase = [&](auto par, int p) __attribute__((always_inline)) {
             constexpr int PAR = decltype(par)::value;

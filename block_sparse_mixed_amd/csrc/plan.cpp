@@ -87,7 +87,6 @@ extern "C" da2_status da2_plan(const da2_config* cfg, da2_plan_t** out) {
     L.q8 = take(B * N * T * P);
     L.k8 = take(B * N * T * P);
     L.qb = take(B * N * T * P * 2);
-    L.kb = take(B * N * T * P * 2);
     L.v8t = take(B * N * P * T);
     L.e8 = take(3 * B * N);
     L.q4 = take(B * N * T * P / 2);
@@ -147,7 +146,6 @@ extern "C" da2_status da2_plan_info(const da2_plan_t* plan, da2_plan_info_t* out
     i.off_lo = L.lo;
     i.off_status = L.status;
     i.off_qb = L.qb;
-    i.off_kb = L.kb;
     i.off_bias = L.bias;
     *out = i;
     return DA2_OK;
