@@ -24,6 +24,9 @@ field is null.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan480p]
        [--no-cpu-baseline]
        python bench.py --copy-calibration   (counter calibration run only)
+       python bench.py --sweep              (budget sweep on the Wan-480p shape, one
+                                             JSON line per point, with the error
+                                             against dense fp32 attention)
 """
 
 from __future__ import annotations
@@ -54,6 +57,10 @@ def parse():
     ap.add_argument("--workload", default="wan480p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=12)
+    ap.add_argument("--sweep", action="store_true",
+                    help="budget sweep on the Wan-480p shape: time and error vs dense fp32 per point")
+    ap.add_argument("--sweep-rows", type=int, default=2048,
+                    help="query rows per head sampled for the error against dense attention")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a streaming kernel of known size (read 1 GiB, write 1 GiB), for counter scaling")
     return ap.parse_args()
@@ -144,10 +151,82 @@ def cpu_baseline(w, q, k, v, n_blocks_sample):
     }
 
 
+def dense_error(q, k, v, out, tau, rows_per_head, seed=0):
+    """Error of `out` against dense fp32 softmax attention over the same bf16
+    inputs, on a seeded sample of query rows of every head: max-abs,
+    relative L2 and mean cosine similarity."""
+    import torch
+    B, H, N, d = q.shape
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    rows = torch.randperm(N, generator=g)[:rows_per_head].to(q.device)
+    num = den = 0.0
+    worst = 0.0
+    cos = []
+    for b in range(B):
+        for h in range(H):
+            qs = q[b, h, rows].float()
+            logits = (qs @ k[b, h].float().t()) * tau
+            ref = torch.softmax(logits, dim=-1) @ v[b, h].float()
+            got = out[b, h, rows].float()
+            diff = got - ref
+            worst = max(worst, float(diff.abs().max()))
+            num += float((diff * diff).sum())
+            den += float((ref * ref).sum())
+            cos.append(torch.nn.functional.cosine_similarity(got, ref, dim=-1).mean().item())
+    return {"max_abs": worst, "rel_l2": (num / den) ** 0.5, "mean_cos": sum(cos) / len(cos),
+            "rows_per_head": int(rows.numel())}
+
+
+def sweep(args):
+    import torch
+
+    import block_sparse_mixed_amd as da2
+    import synthetic as S
+    base = S.WORKLOADS[args.workload]
+    q, k, v = (t.to("cuda:0") for t in S.make_qkv(base))
+    for hi, lo in S.SWEEP_POINTS:
+        w = S.with_budgets(base, hi, lo)
+        cfg = da2.make_config(w.batch, w.heads, w.frames, w.grid_h, w.grid_w, w.head_dim, w.win_h, w.win_w,
+                              w.budget_hi, w.budget_lo, out_dtype=da2.DA2_OUT_FP32)
+        plan = da2.da2_plan(cfg)
+        info = plan.info
+        ws = plan.workspace(q.device)
+        out = torch.empty(w.batch, w.heads, w.tokens, w.head_dim, dtype=torch.float32, device=q.device)
+        stream = torch.cuda.current_stream(q.device)
+        for _ in range(args.warmup):
+            da2.da2_prepare(plan, q, k, v, ws, stream)
+            da2.da2_attention(plan, ws, out, stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            da2.da2_prepare(plan, q, k, v, ws, stream)
+        ev[1].record(stream)
+        for _ in range(args.steps):
+            da2.da2_attention(plan, ws, out, stream)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        prep_ms = ev[0].elapsed_time(ev[1]) / args.steps
+        attn_ms = ev[1].elapsed_time(ev[2]) / args.steps
+        dense, f_hi, f_lo = flops(w, info.n_blocks, info.n_hi, info.n_lo)
+        t_star = f_hi / P_FP8 + f_lo / P_FP4
+        err = dense_error(q, k, v, out, info.tau, args.sweep_rows)
+        print(json.dumps({"sweep_point": {"budget_hi": hi, "budget_lo": lo, "n_hi": info.n_hi, "n_lo": info.n_lo},
+                          "attention_ms": attn_ms, "prepare_ms": prep_ms,
+                          "dense_equiv_tflops": dense / ((attn_ms + prep_ms) / 1e3) / 1e12,
+                          "attention_executed_tflops": (f_hi + f_lo) / (attn_ms / 1e3) / 1e12,
+                          "blended_roofline_frac": t_star / (attn_ms / 1e3) if f_hi + f_lo > 0 else None,
+                          "error_vs_dense_fp32": err, "workload": base.name}), flush=True)
+        del ws, out, plan
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.sweep:
+        sweep(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "

@@ -96,7 +96,15 @@ def test_wan_shape_sampled(da2):
     _full_parity(da2, S.WAN480, heads=[0, 7], att_blocks=[0, 3, 15, 16, 170, 335])
 
 
-@pytest.mark.parametrize("hi,lo", [(0.05, 0.0), (0.25, 0.4), (1.0, 0.0), (0.0, 1.0)])
+def test_hunyuan_shape_sampled(da2):
+    # the largest shape: 24 heads x 118800 tokens, 990 blocks (rows of windows
+    # partial in y); codes/labels for the first and last head, outputs on
+    # sampled query blocks including a partial window (29) and the last block
+    _full_parity(da2, S.HUNYUAN720, heads=[0, 23], att_blocks=[0, 29, 500, 989])
+
+
+@pytest.mark.parametrize("hi,lo", [(0.05, 0.0), (0.05, 0.4), (0.1, 0.2), (0.25, 0.2), (0.25, 0.4), (1.0, 0.0),
+                                   (0.0, 1.0)])
 def test_wan_sweep_points_sampled(da2, hi, lo):
     w = S.with_budgets(S.WAN480, hi, lo)
     _full_parity(da2, w, heads=[3], att_blocks=[0, 15, 200])
