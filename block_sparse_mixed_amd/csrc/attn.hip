@@ -31,7 +31,10 @@
 //   The query block's Q operands (bf16 and E2M1) sit in LDS for the whole
 //   kernel. K and V^T of a tile travel by direct global->LDS DMA into
 //   separate two-slot pools: K of tile p+1 and V^T of tile p-1 are issued at
-//   the start of phase p. At the end the teams' (max, sum, accumulator) triples merge
+//   the start of phase p by the team running the softmax (a DMA instruction
+//   holds only the wave that issues it, so the matrix wave sharing its SIMD
+//   keeps issuing). The tile list entries each team needs travel in scalar
+//   registers, read from LDS one trip ahead. At the end the teams' (max, sum, accumulator) triples merge
 //   exactly: their maxima are integers, so the rescale factors are powers of
 //   two. Padded key slots are excluded by starting the QK^T accumulator at a
 //   per-slot bias (0 or -inf) that travels with K.
@@ -87,6 +90,7 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
+constexpr int kTeamWaves = kWaves / 2;
 constexpr int kFmtFp8 = 0;
 constexpr int kFmtFp4 = 4;
 constexpr float kLog2E = 1.4426950408889634f;
@@ -204,25 +208,20 @@ __device__ __forceinline__ Tile tile_from(const AttnArgs& a, const uint8_t* __re
     return t;
 }
 
-template <int PH>
-__device__ __forceinline__ Tile tile_at(const AttnArgs& a, const uint8_t* __restrict__ ws, const int32_t* tl, int bh,
-                                        int idx) {
-    return tile_from<PH>(a, ws, bh, tl[idx]);
-}
-
-// K part of a tile into a K slot, spread over the eight waves.
+// K part of a tile into a K slot, spread over the four waves of one team
+// (w = the wave's index in its team).
 template <int PH>
 __device__ __forceinline__ void dma_k(const Tile& t, uint8_t* slot, int w, int lane, const DmaOffsets& o) {
     if constexpr (PH == kHi) {
 #pragma unroll
-        for (int n = 0; n < 16 / kWaves; ++n) {
-            const int wr = w + kWaves * n;   // 16 KiB of E4M3 K: 8 key rows per wave row
+        for (int n = 0; n < 16 / kTeamWaves; ++n) {
+            const int wr = w + kTeamWaves * n;   // 16 KiB of E4M3 K: 8 key rows per wave row
             dma16(t.k + wr * 1024 + (o.k8f ^ (((wr >> 1) & 3) << 5)), slot + wr * 1024);
         }
     } else {
 #pragma unroll
-        for (int n = 0; n < 8 / kWaves; ++n) {
-            const int wr = w + kWaves * n;   // 8 KiB of E2M1 K
+        for (int n = 0; n < 8 / kTeamWaves; ++n) {
+            const int wr = w + kTeamWaves * n;   // 8 KiB of E2M1 K
             dma16(t.k + wr * 1024 + (o.k4 ^ ((wr & 2) << 4)), slot + wr * 1024);
         }
         if (w == 1 && lane < 32) dma16(t.ks + lane * 16, slot + kKScale);
@@ -230,19 +229,19 @@ __device__ __forceinline__ void dma_k(const Tile& t, uint8_t* slot, int w, int l
     if (w == 0 && lane < 32) dma16(reinterpret_cast<const uint8_t*>(t.bias) + lane * 16, slot + kKBias);
 }
 
-// V part of a tile into a V slot.
+// V part of a tile into a V slot, spread over the four waves of one team.
 template <int PH>
 __device__ __forceinline__ void dma_v(const Tile& t, uint8_t* slot, int w, int lane, const DmaOffsets& o) {
     if constexpr (PH == kHi) {
 #pragma unroll
-        for (int n = 0; n < 16 / kWaves; ++n) {
-            const int wr = w + kWaves * n;   // 16 KiB of E4M3 V^T
+        for (int n = 0; n < 16 / kTeamWaves; ++n) {
+            const int wr = w + kTeamWaves * n;   // 16 KiB of E4M3 V^T
             dma16(t.v + wr * 1024 + o.v8, slot + wr * 1024);
         }
     } else {
 #pragma unroll
-        for (int n = 0; n < 8 / kWaves; ++n) {
-            const int wr = w + kWaves * n;   // 8 KiB of E2M1 V^T
+        for (int n = 0; n < 8 / kTeamWaves; ++n) {
+            const int wr = w + kTeamWaves * n;   // 8 KiB of E2M1 V^T
             dma16(t.v + wr * 1024 + o.v4, slot + wr * 1024);
         }
         if (w == 3 && lane < 32) dma16(t.vs + lane * 16, slot + kVScale);
@@ -698,23 +697,22 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
     };
     auto section = [&](auto ph, int base, int n) __attribute__((always_inline)) {
         constexpr int PH = decltype(ph)::value;
-        auto tile = [&](int j) __attribute__((always_inline)) { return tile_at<PH>(a, ws, tl, bh, base + j); };
-        auto fetch = [&](auto par, int p) __attribute__((always_inline)) {
+        // Packed list entry of tile j of this section. The index wraps inside
+        // the list array; an entry outside the section is never used.
+        auto entry = [&](int j) __attribute__((always_inline)) { return tl[(base + j) & (DA2_MAX_BLOCKS - 1)]; };
+        // ek, ev: entries of K(p+1) and V(p-1), already wave-uniform
+        auto fetch = [&](auto par, int p, int32_t ek, int32_t ev) __attribute__((always_inline)) {
             constexpr int PAR = decltype(par)::value;
             // lane offsets recomputed here (a handful of ALU ops) rather than
             // kept live across the loop, where they would be spilled
             const int ln = fresh_lane();
             const DmaOffsets o = dma_offsets(ln);
-            // Both list entries are read before any DMA is issued (one LDS
-            // round trip); indices wrap inside the list array, and an entry
-            // outside the section is never used.
-            const int32_t ek = tl[(base + p + 1) & (DA2_MAX_BLOCKS - 1)];
-            const int32_t ev = tl[(base + p - 1) & (DA2_MAX_BLOCKS - 1)];
             // K(p+1) and V(p-1) both go to the slots of parity PAR ^ 1
-            if (p + 1 < n) dma_k<PH>(tile_from<PH>(a, ws, bh, ek), PAR ? kslot0 : kslot1, w, ln, o);
-            if (p >= 1 && p - 1 < n) dma_v<PH>(tile_from<PH>(a, ws, bh, ev), PAR ? vslot0 : vslot1, w, ln, o);
+            if (p + 1 < n) dma_k<PH>(tile_from<PH>(a, ws, bh, ek), PAR ? kslot0 : kslot1, wq, ln, o);
+            if (p >= 1 && p - 1 < n) dma_v<PH>(tile_from<PH>(a, ws, bh, ev), PAR ? vslot0 : vslot1, wq, ln, o);
         };
-        auto mma_phase = [&](auto par, int p) __attribute__((always_inline)) {
+        // ev: entry of tile p-2, whose PV runs here
+        auto mma_phase = [&](auto par, int p, int32_t ev) __attribute__((always_inline)) {
             constexpr int PAR = decltype(par)::value;
             // the lane coordinates are recomputed here, not kept live
             const int ln = fresh_lane();
@@ -722,7 +720,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
             // Q operands for this phase's QK^T are read first, under the PV
             QOps qo;
             if (p < n) load_q<PH>(st, qo, r, g4);
-            if (p >= 2) pv<PH>(st, PAR ? vslot1 : vslot0, pop, psc, PH == kHi ? tile(p - 2).e_v : 0, r, g4);
+            if (p >= 2) pv<PH>(st, PAR ? vslot1 : vslot0, pop, psc, PH == kHi ? tile_from<PH>(a, ws, bh, ev).e_v : 0, r, g4);
             if (p < n) {
                 qk<PH>(PAR ? kslot1 : kslot0, qo, s, r, g4);
             } else {
@@ -733,9 +731,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
                     for (int t = 0; t < 8; ++t) s[u][t] = (v4f){0.f, 0.f, 0.f, 0.f};
             }
         };
-        auto softmax_phase = [&](int p) __attribute__((always_inline)) {
+        // ek: entry of tile p-1, whose softmax runs here
+        auto softmax_phase = [&](int p, int32_t ek) __attribute__((always_inline)) {
             if (p >= 1 && p - 1 < n) {
-                softmax<PH>(st, s, PH == kHi ? tile(p - 1).e_k : 0, pop, psc);
+                softmax<PH>(st, s, PH == kHi ? tile_from<PH>(a, ws, bh, ek).e_k : 0, pop, psc);
             } else {
                 // defined on every path, so the previous P is dead here
 #pragma unroll
@@ -746,34 +745,61 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
                 }
             }
         };
+        // a list entry read from LDS at the start of a phase becomes a scalar
+        // at its end, after the phase's work has hidden the LDS latency
+        auto uniform = [&](int32_t v) __attribute__((always_inline)) {
+            fence();
+            return (int32_t)__builtin_amdgcn_readfirstlane(v);
+        };
         using Even = std::integral_constant<int, 0>;
         using Odd = std::integral_constant<int, 1>;
-        // the section's first K tile
-        {
+        // the section's first K tile (team 1, which fetches in the even phases)
+        if (team == 1) {
             const int ln = fresh_lane();
-            dma_k<PH>(tile(0), kslot0, w, ln, dma_offsets(ln));
-            sync();
+            dma_k<PH>(tile_from<PH>(a, ws, bh, (int32_t)__builtin_amdgcn_readfirstlane(entry(0))), kslot0, wq, ln,
+                      dma_offsets(ln));
         }
+        // Each team owns the tiles j of its parity and carries three list
+        // entries in scalar registers: e_prev (tile j-2, whose PV runs in
+        // phase j), e_cur (tile j: softmax and V fetch in phase j+1) and
+        // e_next (tile j+2: K fetch in phase j+1). The entry of tile j+4 is
+        // read during phase j+1.
+        int32_t e_prev = 0;
+        int32_t e_cur = __builtin_amdgcn_readfirstlane(entry(team == 0 ? 0 : -1));
+        int32_t e_next = __builtin_amdgcn_readfirstlane(entry(team == 0 ? 2 : 1));
+        sync();
+        // Each phase's fetch is issued by the team running the softmax, at
+        // the start of the phase.
         const int n_phases = n + 2;
         if (team == 0) {
             for (int p = 0; p < n_phases; p += 2) {
-                fetch(Even{}, p);
-                mma_phase(Even{}, p);
+                // tile j = p: e_prev = E[p-2], e_cur = E[p], e_next = E[p+2]
+                mma_phase(Even{}, p, e_prev);
                 sync();
                 if (p + 1 < n_phases) {
-                    fetch(Odd{}, p + 1);
-                    softmax_phase(p + 1);
+                    const int32_t ahead = entry(p + 4);
+                    fetch(Odd{}, p + 1, e_next, e_cur);
+                    softmax_phase(p + 1, e_cur);
+                    const int32_t e_new = uniform(ahead);
                     sync();
+                    e_prev = e_cur;
+                    e_cur = e_next;
+                    e_next = e_new;
                 }
             }
         } else {
             for (int p = 0; p < n_phases; p += 2) {
-                fetch(Even{}, p);
-                softmax_phase(p);
+                // tile j = p - 1: e_cur = E[p-1], e_next = E[p+1]
+                const int32_t ahead = entry(p + 3);
+                fetch(Even{}, p, e_next, e_cur);
+                softmax_phase(p, e_cur);
+                const int32_t e_new = uniform(ahead);
                 sync();
+                e_prev = e_cur;
+                e_cur = e_next;
+                e_next = e_new;
                 if (p + 1 < n_phases) {
-                    fetch(Odd{}, p + 1);
-                    mma_phase(Odd{}, p + 1);
+                    mma_phase(Odd{}, p + 1, e_prev);
                     sync();
                 }
             }
