@@ -67,6 +67,7 @@
 //   fp8:  slot = 64*(t/4) + 16*(r/4) + 4*(t%4) + r%4
 //   fp4:  slot = 32*(r/4) + 4*t + r%4          (k-block g = slots 32g..32g+31)
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 
@@ -143,6 +144,16 @@ __device__ __forceinline__ int fresh_lane() {
 // Scheduling fence: nothing moves across it, which bounds register live ranges.
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+// f(std::integral_constant<int, i>) for i = 0 .. N-1
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 __device__ __forceinline__ void dma16(const void* gsrc, uint8_t* ldst) {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
                                      (__attribute__((address_space(3))) void*)ldst, 16, 0, 0);
@@ -208,44 +219,57 @@ __device__ __forceinline__ Tile tile_from(const AttnArgs& a, const uint8_t* __re
     return t;
 }
 
-// K part of a tile into a K slot, spread over the four waves of one team
-// (w = the wave's index in its team).
+// A phase's fetch, K(p+1) and V^T(p-1), is spread over the four waves of one
+// team as a short list of DMA items per wave (w = the wave's index in its
+// team): fp8 tiles 4 K rows, 4 V rows and the K bias; MXFP4 tiles 2 K rows,
+// 2 V rows, the K scales and bias, and the V scales. A row is 1 KiB, one
+// instruction over the wave's 64 lanes.
 template <int PH>
-__device__ __forceinline__ void dma_k(const Tile& t, uint8_t* slot, int w, int lane, const DmaOffsets& o) {
-    if constexpr (PH == kHi) {
-#pragma unroll
-        for (int n = 0; n < 16 / kTeamWaves; ++n) {
-            const int wr = w + kTeamWaves * n;   // 16 KiB of E4M3 K: 8 key rows per wave row
-            dma16(t.k + wr * 1024 + (o.k8f ^ (((wr >> 1) & 3) << 5)), slot + wr * 1024);
+constexpr int kFetchItems = PH == kHi ? 9 : 6;
+
+template <int PH, int I>
+__device__ __forceinline__ void fetch_item(const Tile& tk, uint8_t* kslot, bool do_k, const Tile& tv, uint8_t* vslot,
+                                           bool do_v, int w, int lane, const DmaOffsets& o) {
+    constexpr int kRows = (PH == kHi ? 16 : 8) / kTeamWaves;
+    if constexpr (I < kRows) {
+        const int wr = w + kTeamWaves * I;
+        if (do_k) {
+            if constexpr (PH == kHi)   // 16 KiB of E4M3 K: 8 key rows per 1 KiB row
+                dma16(tk.k + wr * 1024 + (o.k8f ^ (((wr >> 1) & 3) << 5)), kslot + wr * 1024);
+            else                       // 8 KiB of E2M1 K
+                dma16(tk.k + wr * 1024 + (o.k4 ^ ((wr & 2) << 4)), kslot + wr * 1024);
+        }
+    } else if constexpr (I < 2 * kRows) {
+        const int wr = w + kTeamWaves * (I - kRows);
+        if (do_v) {
+            if constexpr (PH == kHi)   // 16 KiB of E4M3 V^T
+                dma16(tv.v + wr * 1024 + o.v8, vslot + wr * 1024);
+            else                       // 8 KiB of E2M1 V^T
+                dma16(tv.v + wr * 1024 + o.v4, vslot + wr * 1024);
+        }
+    } else if constexpr (I == 2 * kRows) {
+        if (do_k) {
+            if constexpr (PH == kLo)
+                if (w == 1 && lane < 32) dma16(tk.ks + lane * 16, kslot + kKScale);
+            if (w == 0 && lane < 32) dma16(reinterpret_cast<const uint8_t*>(tk.bias) + lane * 16, kslot + kKBias);
         }
     } else {
-#pragma unroll
-        for (int n = 0; n < 8 / kTeamWaves; ++n) {
-            const int wr = w + kTeamWaves * n;   // 8 KiB of E2M1 K
-            dma16(t.k + wr * 1024 + (o.k4 ^ ((wr & 2) << 4)), slot + wr * 1024);
-        }
-        if (w == 1 && lane < 32) dma16(t.ks + lane * 16, slot + kKScale);
+        static_assert(PH == kLo && I == 2 * kRows + 1, "fetch item");
+        if (do_v && w == 3 && lane < 32) dma16(tv.vs + lane * 16, vslot + kVScale);
     }
-    if (w == 0 && lane < 32) dma16(reinterpret_cast<const uint8_t*>(t.bias) + lane * 16, slot + kKBias);
 }
 
-// V part of a tile into a V slot, spread over the four waves of one team.
+// All of a team's K items of one tile (the first tile of a section).
 template <int PH>
-__device__ __forceinline__ void dma_v(const Tile& t, uint8_t* slot, int w, int lane, const DmaOffsets& o) {
-    if constexpr (PH == kHi) {
-#pragma unroll
-        for (int n = 0; n < 16 / kTeamWaves; ++n) {
-            const int wr = w + kTeamWaves * n;   // 16 KiB of E4M3 V^T
-            dma16(t.v + wr * 1024 + o.v8, slot + wr * 1024);
-        }
-    } else {
-#pragma unroll
-        for (int n = 0; n < 8 / kTeamWaves; ++n) {
-            const int wr = w + kTeamWaves * n;   // 8 KiB of E2M1 V^T
-            dma16(t.v + wr * 1024 + o.v4, slot + wr * 1024);
-        }
-        if (w == 3 && lane < 32) dma16(t.vs + lane * 16, slot + kVScale);
-    }
+__device__ __forceinline__ void dma_k(const Tile& t, uint8_t* slot, int w, int lane, const DmaOffsets& o) {
+    auto all = [&](auto... is) __attribute__((always_inline)) {
+        (fetch_item<PH, decltype(is)::value>(t, slot, true, t, nullptr, false, w, lane, o), ...);
+    };
+    if constexpr (PH == kHi)
+        all(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{},
+            std::integral_constant<int, 3>{}, std::integral_constant<int, 8>{});
+    else
+        all(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 4>{});
 }
 
 struct WaveState {
@@ -433,8 +457,12 @@ __device__ __forceinline__ float cross4max(float v) {
 // two, and mref moved to m.
 constexpr float kMaxLead = 64.0f;
 
-template <int PH>
-__device__ __forceinline__ void softmax(WaveState& st, const v4f (&s)[2][8], int e_k, v8i (&pop)[2], int (&psc)[2]) {
+// hook(i) issues fetch item i of the phase (nothing for i past the last):
+// the items are spread through the softmax so that each DMA instruction's
+// hold on this wave is interleaved with the wave's own arithmetic.
+template <int PH, class Hook>
+__device__ __forceinline__ void softmax(WaveState& st, const v4f (&s)[2][8], int e_k, v8i (&pop)[2], int (&psc)[2],
+                                        Hook&& hook) {
     const float cs = PH == kHi ? ldexpf(st.c_hi_q, e_k) : st.c_lo;
     float gmax[2], mnew[2];
 #pragma unroll
@@ -442,6 +470,7 @@ __device__ __forceinline__ void softmax(WaveState& st, const v4f (&s)[2][8], int
         gmax[u] = max32(s[u]);                           // this lane's 32 keys (raw scores)
         mnew[u] = fmaxf(st.m[u], ceilf(cross4max(gmax[u]) * cs));
     }
+    hook(std::integral_constant<int, 0>{});
     if (!(st.mref[0] >= mnew[0] - kMaxLead) || !(st.mref[1] >= mnew[1] - kMaxLead)) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -452,18 +481,22 @@ __device__ __forceinline__ void softmax(WaveState& st, const v4f (&s)[2][8], int
             st.mref[u] = mnew[u];
         }
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    static_for<2>([&](auto uc) __attribute__((always_inline)) {
+        constexpr int U = decltype(uc)::value;
+        constexpr int u = U;
         if constexpr (PH == kHi) {
             const float off = 8.0f - mnew[u];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
+            static_for<8>([&](auto tc) __attribute__((always_inline)) {
+                constexpr int t = decltype(tc)::value;
                 pop[u][t] = (int)pack_fp8x4(__builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][0], cs, off)),
                                             __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][1], cs, off)),
                                             __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][2], cs, off)),
                                             __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][3], cs, off)));
-                if ((t & 1) == 1) fence();
-            }
+                if constexpr ((t & 1) == 1) {
+                    hook(std::integral_constant<int, 1 + 4 * U + (t >> 1)>{});
+                    fence();
+                }
+            });
             psc[u] = 127 + (int)(mnew[u] - st.mref[u]);      // 127 .. 127 + kMaxLead
         } else {
             // MX group of P = this lane's 32 keys: scale 2^F, F the smallest
@@ -471,19 +504,20 @@ __device__ __forceinline__ void softmax(WaveState& st, const v4f (&s)[2][8], int
             const bool any = gmax[u] > -__builtin_huge_valf();
             const float F = any ? ceilf(gmax[u] * cs - kLog2Six) : 0.0f;
             const float off = -F;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
+            static_for<4>([&](auto dc) __attribute__((always_inline)) {
+                constexpr int d = decltype(dc)::value;
                 float v[8];
 #pragma unroll
                 for (int q = 0; q < 8; ++q)
                     v[q] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][2 * d + (q >> 2)][q & 3], cs, off));
                 pop[u][d] = (int)pack_fp4x8(v);
+                hook(std::integral_constant<int, 1 + 4 * U + d>{});
                 fence();
-            }
+            });
             const int sc = any ? (int)(F - st.mref[u]) + 8 + 127 : 0;
             psc[u] = min(254, max(0, sc));
         }
-    }
+    });
     st.m[0] = mnew[0];
     st.m[1] = mnew[1];
 }
@@ -700,17 +734,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
         // Packed list entry of tile j of this section. The index wraps inside
         // the list array; an entry outside the section is never used.
         auto entry = [&](int j) __attribute__((always_inline)) { return tl[(base + j) & (DA2_MAX_BLOCKS - 1)]; };
-        // ek, ev: entries of K(p+1) and V(p-1), already wave-uniform
-        auto fetch = [&](auto par, int p, int32_t ek, int32_t ev) __attribute__((always_inline)) {
-            constexpr int PAR = decltype(par)::value;
-            // lane offsets recomputed here (a handful of ALU ops) rather than
-            // kept live across the loop, where they would be spilled
-            const int ln = fresh_lane();
-            const DmaOffsets o = dma_offsets(ln);
-            // K(p+1) and V(p-1) both go to the slots of parity PAR ^ 1
-            if (p + 1 < n) dma_k<PH>(tile_from<PH>(a, ws, bh, ek), PAR ? kslot0 : kslot1, wq, ln, o);
-            if (p >= 1 && p - 1 < n) dma_v<PH>(tile_from<PH>(a, ws, bh, ev), PAR ? vslot0 : vslot1, wq, ln, o);
-        };
+        const int32_t e_first = __builtin_amdgcn_readfirstlane(entry(0));
         // ev: entry of tile p-2, whose PV runs here
         auto mma_phase = [&](auto par, int p, int32_t ev) __attribute__((always_inline)) {
             constexpr int PAR = decltype(par)::value;
@@ -731,11 +755,32 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
                     for (int t = 0; t < 8; ++t) s[u][t] = (v4f){0.f, 0.f, 0.f, 0.f};
             }
         };
-        // ek: entry of tile p-1, whose softmax runs here
-        auto softmax_phase = [&](int p, int32_t ek) __attribute__((always_inline)) {
+        // ek: entry of tile p-1, whose softmax runs here. The phase's fetch
+        // (fk, fv: entries of K(p+1) and V(p-1), already wave-uniform) is
+        // issued from inside the softmax, item by item; K(p+1) and V(p-1)
+        // both go to the slots of parity PAR ^ 1.
+        auto softmax_phase = [&](auto par, int p, int32_t ek, int32_t fk, int32_t fv) __attribute__((always_inline)) {
+            constexpr int PAR = decltype(par)::value;
+            // lane offsets recomputed here (a handful of ALU ops) rather than
+            // kept live across the loop, where they would be spilled
+            const int ln = fresh_lane();
+            const DmaOffsets o = dma_offsets(ln);
+            // Outside the section (the first and last phases) the fetch
+            // repeats tile 0 into the slots of parity PAR ^ 1, which no one
+            // reads then: every phase issues the same instructions, with no
+            // branch per item.
+            const Tile tk = tile_from<PH>(a, ws, bh, p + 1 < n ? fk : e_first);
+            const Tile tv = tile_from<PH>(a, ws, bh, p >= 1 && p - 1 < n ? fv : e_first);
+            uint8_t* ks = PAR ? kslot0 : kslot1;
+            uint8_t* vs = PAR ? vslot0 : vslot1;
+            auto hook = [&](auto item) __attribute__((always_inline)) {
+                constexpr int I = decltype(item)::value;
+                if constexpr (I < kFetchItems<PH>) fetch_item<PH, I>(tk, ks, true, tv, vs, true, wq, ln, o);
+            };
             if (p >= 1 && p - 1 < n) {
-                softmax<PH>(st, s, PH == kHi ? tile_from<PH>(a, ws, bh, ek).e_k : 0, pop, psc);
+                softmax<PH>(st, s, PH == kHi ? tile_from<PH>(a, ws, bh, ek).e_k : 0, pop, psc, hook);
             } else {
+                static_for<kFetchItems<PH>>(hook);
                 // defined on every path, so the previous P is dead here
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
@@ -756,8 +801,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
         // the section's first K tile (team 1, which fetches in the even phases)
         if (team == 1) {
             const int ln = fresh_lane();
-            dma_k<PH>(tile_from<PH>(a, ws, bh, (int32_t)__builtin_amdgcn_readfirstlane(entry(0))), kslot0, wq, ln,
-                      dma_offsets(ln));
+            dma_k<PH>(tile_from<PH>(a, ws, bh, e_first), kslot0, wq, ln, dma_offsets(ln));
         }
         // Each team owns the tiles j of its parity and carries three list
         // entries in scalar registers: e_prev (tile j-2, whose PV runs in
@@ -768,8 +812,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
         int32_t e_cur = __builtin_amdgcn_readfirstlane(entry(team == 0 ? 0 : -1));
         int32_t e_next = __builtin_amdgcn_readfirstlane(entry(team == 0 ? 2 : 1));
         sync();
-        // Each phase's fetch is issued by the team running the softmax, at
-        // the start of the phase.
+        // Each phase's fetch is issued by the team running the softmax,
+        // spread through it.
         const int n_phases = n + 2;
         if (team == 0) {
             for (int p = 0; p < n_phases; p += 2) {
@@ -778,8 +822,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
                 sync();
                 if (p + 1 < n_phases) {
                     const int32_t ahead = entry(p + 4);
-                    fetch(Odd{}, p + 1, e_next, e_cur);
-                    softmax_phase(p + 1, e_cur);
+                    softmax_phase(Odd{}, p + 1, e_cur, e_next, e_cur);
                     const int32_t e_new = uniform(ahead);
                     sync();
                     e_prev = e_cur;
@@ -791,8 +834,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
             for (int p = 0; p < n_phases; p += 2) {
                 // tile j = p - 1: e_cur = E[p-1], e_next = E[p+1]
                 const int32_t ahead = entry(p + 3);
-                fetch(Even{}, p, e_next, e_cur);
-                softmax_phase(p, e_cur);
+                softmax_phase(Even{}, p, e_cur, e_next, e_cur);
                 const int32_t e_new = uniform(ahead);
                 sync();
                 e_prev = e_cur;
