@@ -485,7 +485,9 @@ __device__ __forceinline__ void softmax(WaveState& st, const v4f (&s)[2][8], int
         constexpr int U = decltype(uc)::value;
         constexpr int u = U;
         if constexpr (PH == kHi) {
-            const float off = 8.0f - mnew[u];
+            // finite also while no key has been seen (mnew = -inf): the
+            // scores are then -inf and the codes 0
+            const float off = 8.0f - fmaxf(mnew[u], -__FLT_MAX__);
             static_for<8>([&](auto tc) __attribute__((always_inline)) {
                 constexpr int t = decltype(tc)::value;
                 pop[u][t] = (int)pack_fp8x4(__builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][0], cs, off)),
@@ -497,7 +499,8 @@ __device__ __forceinline__ void softmax(WaveState& st, const v4f (&s)[2][8], int
                     fence();
                 }
             });
-            psc[u] = 127 + (int)(mnew[u] - st.mref[u]);      // 127 .. 127 + kMaxLead
+            // 127 .. 127 + kMaxLead (127 while no key has been seen: both -inf)
+            psc[u] = 127 + (int)fmaxf(mnew[u] - st.mref[u], 0.0f);
         } else {
             // MX group of P = this lane's 32 keys: scale 2^F, F the smallest
             // integer with 2^(gmax cs) <= 6 * 2^F; codes RNE(2^(x - F)).
@@ -664,6 +667,20 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
             tl[i] = (int32_t)e;
         }
     }
+    // The key and value slots start zeroed, so that every byte in them is a
+    // finite code or scale: the empty tile's PV reads value slots that no
+    // fetch has written yet (with P = 0).
+    {
+        const uint4 z = {0u, 0u, 0u, 0u};
+        for (int i = tid; i < kKSlot / 16; i += kThreads) {
+            reinterpret_cast<uint4*>(kslot0)[i] = z;
+            reinterpret_cast<uint4*>(kslot1)[i] = z;
+        }
+        for (int i = tid; i < kVSlot / 16; i += kThreads) {
+            reinterpret_cast<uint4*>(vslot0)[i] = z;
+            reinterpret_cast<uint4*>(vslot1)[i] = z;
+        }
+    }
     __syncthreads();
 
     // the query block's Q operands (swizzled rows)
@@ -729,13 +746,30 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
+    // The empty key tile: codes of the section's first tile, bias row
+    // n_blocks (all -inf). Its scores are -inf, so its softmax leaves the
+    // running max and the accumulator untouched and its P codes are zero,
+    // which makes its PV a no-op: the phases before and after a section's
+    // tiles run the same code as the others, on it.
+    const float* empty_bias = reinterpret_cast<const float*>(ws + a.L.bias) + (uint64_t)nb * DA2_TILE;
     auto section = [&](auto ph, int base, int n) __attribute__((always_inline)) {
         constexpr int PH = decltype(ph)::value;
         // Packed list entry of tile j of this section. The index wraps inside
         // the list array; an entry outside the section is never used.
         auto entry = [&](int j) __attribute__((always_inline)) { return tl[(base + j) & (DA2_MAX_BLOCKS - 1)]; };
         const int32_t e_first = __builtin_amdgcn_readfirstlane(entry(0));
-        // ev: entry of tile p-2, whose PV runs here
+        auto real = [&](int j) __attribute__((always_inline)) { return j >= 0 && j < n; };
+        // tile j of the section, or the empty tile
+        auto tile = [&](int j, int32_t e) __attribute__((always_inline)) {
+            Tile t = tile_from<PH>(a, ws, bh, real(j) ? e : e_first);
+            if (!real(j)) {
+                t.bias = empty_bias;
+                t.e_k = 0;
+                t.e_v = 0;
+            }
+            return t;
+        };
+        // phase p of the matrix team: PV(p-2) and QK^T(p); ev: entry of tile p-2
         auto mma_phase = [&](auto par, int p, int32_t ev) __attribute__((always_inline)) {
             constexpr int PAR = decltype(par)::value;
             // the lane coordinates are recomputed here, not kept live
@@ -743,52 +777,28 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
             const int r = ln & 15, g4 = ln >> 4;
             // Q operands for this phase's QK^T are read first, under the PV
             QOps qo;
-            if (p < n) load_q<PH>(st, qo, r, g4);
-            if (p >= 2) pv<PH>(st, PAR ? vslot1 : vslot0, pop, psc, PH == kHi ? tile_from<PH>(a, ws, bh, ev).e_v : 0, r, g4);
-            if (p < n) {
-                qk<PH>(PAR ? kslot1 : kslot0, qo, s, r, g4);
-            } else {
-                // defined on every path, so the previous scores are dead here
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) s[u][t] = (v4f){0.f, 0.f, 0.f, 0.f};
-            }
+            load_q<PH>(st, qo, r, g4);
+            pv<PH>(st, PAR ? vslot1 : vslot0, pop, psc, tile(p - 2, ev).e_v, r, g4);
+            qk<PH>(PAR ? kslot1 : kslot0, qo, s, r, g4);
         };
-        // ek: entry of tile p-1, whose softmax runs here. The phase's fetch
-        // (fk, fv: entries of K(p+1) and V(p-1), already wave-uniform) is
-        // issued from inside the softmax, item by item; K(p+1) and V(p-1)
-        // both go to the slots of parity PAR ^ 1.
+        // phase p of the other team: the softmax of tile p-1 (entry ek), with
+        // the phase's fetch (fk, fv: entries of K(p+1) and V(p-1)) issued from
+        // inside it; K(p+1) and V(p-1) both go to the slots of parity PAR ^ 1.
         auto softmax_phase = [&](auto par, int p, int32_t ek, int32_t fk, int32_t fv) __attribute__((always_inline)) {
             constexpr int PAR = decltype(par)::value;
             // lane offsets recomputed here (a handful of ALU ops) rather than
             // kept live across the loop, where they would be spilled
             const int ln = fresh_lane();
             const DmaOffsets o = dma_offsets(ln);
-            // Outside the section (the first and last phases) the fetch
-            // repeats tile 0 into the slots of parity PAR ^ 1, which no one
-            // reads then: every phase issues the same instructions, with no
-            // branch per item.
-            const Tile tk = tile_from<PH>(a, ws, bh, p + 1 < n ? fk : e_first);
-            const Tile tv = tile_from<PH>(a, ws, bh, p >= 1 && p - 1 < n ? fv : e_first);
+            const Tile tk = tile(p + 1, fk);
+            const Tile tv = tile(p - 1, fv);
             uint8_t* ks = PAR ? kslot0 : kslot1;
             uint8_t* vs = PAR ? vslot0 : vslot1;
             auto hook = [&](auto item) __attribute__((always_inline)) {
                 constexpr int I = decltype(item)::value;
                 if constexpr (I < kFetchItems<PH>) fetch_item<PH, I>(tk, ks, true, tv, vs, true, wq, ln, o);
             };
-            if (p >= 1 && p - 1 < n) {
-                softmax<PH>(st, s, PH == kHi ? tile_from<PH>(a, ws, bh, ek).e_k : 0, pop, psc, hook);
-            } else {
-                static_for<kFetchItems<PH>>(hook);
-                // defined on every path, so the previous P is dead here
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    psc[u] = 127;
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) pop[u][q] = 0;
-                }
-            }
+            softmax<PH>(st, s, tile(p - 1, ek).e_k, pop, psc, hook);
         };
         // a list entry read from LDS at the start of a phase becomes a scalar
         // at its end, after the phase's work has hidden the LDS latency
@@ -801,7 +811,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
         // the section's first K tile (team 1, which fetches in the even phases)
         if (team == 1) {
             const int ln = fresh_lane();
-            dma_k<PH>(tile_from<PH>(a, ws, bh, e_first), kslot0, wq, ln, dma_offsets(ln));
+            dma_k<PH>(tile(0, e_first), kslot0, wq, ln, dma_offsets(ln));
+        }
+        // before the section: the scores of the empty tile, no P
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            psc[u] = 127;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) pop[u][q] = 0;
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                s[u][t] = (v4f){-__builtin_huge_valf(), -__builtin_huge_valf(), -__builtin_huge_valf(),
+                                -__builtin_huge_valf()};
         }
         // Each team owns the tiles j of its parity and carries three list
         // entries in scalar registers: e_prev (tile j-2, whose PV runs in
@@ -812,23 +833,21 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
         int32_t e_cur = __builtin_amdgcn_readfirstlane(entry(team == 0 ? 0 : -1));
         int32_t e_next = __builtin_amdgcn_readfirstlane(entry(team == 0 ? 2 : 1));
         sync();
-        // Each phase's fetch is issued by the team running the softmax,
-        // spread through it.
-        const int n_phases = n + 2;
+        // n + 2 phases, rounded up to an even count so that every trip of
+        // either team's loop runs one phase of each kind
+        const int n_phases = (n + 3) & ~1;
         if (team == 0) {
             for (int p = 0; p < n_phases; p += 2) {
                 // tile j = p: e_prev = E[p-2], e_cur = E[p], e_next = E[p+2]
                 mma_phase(Even{}, p, e_prev);
                 sync();
-                if (p + 1 < n_phases) {
-                    const int32_t ahead = entry(p + 4);
-                    softmax_phase(Odd{}, p + 1, e_cur, e_next, e_cur);
-                    const int32_t e_new = uniform(ahead);
-                    sync();
-                    e_prev = e_cur;
-                    e_cur = e_next;
-                    e_next = e_new;
-                }
+                const int32_t ahead = entry(p + 4);
+                softmax_phase(Odd{}, p + 1, e_cur, e_next, e_cur);
+                const int32_t e_new = uniform(ahead);
+                sync();
+                e_prev = e_cur;
+                e_cur = e_next;
+                e_next = e_new;
             }
         } else {
             for (int p = 0; p < n_phases; p += 2) {
@@ -840,10 +859,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
                 e_prev = e_cur;
                 e_cur = e_next;
                 e_next = e_new;
-                if (p + 1 < n_phases) {
-                    mma_phase(Odd{}, p + 1, e_prev);
-                    sync();
-                }
+                mma_phase(Odd{}, p + 1, e_prev);
+                sync();
             }
         }
     };

@@ -100,7 +100,7 @@ extern "C" da2_status da2_plan(const da2_config* cfg, da2_plan_t** out) {
     L.hi = take(B * N * (uint64_t)(g.n_hi > 0 ? g.n_hi : 1) * 4);
     L.lo = take(B * N * (uint64_t)(g.n_lo > 0 ? g.n_lo : 1) * 4);
     L.status = take(16);
-    L.bias = take(N * T * 4);
+    L.bias = take((N + 1) * T * 4);   // row N: a tile with no keys (all -inf)
     L.total = off;
 
     da2_plan_t* p = new (std::nothrow) da2_plan_t;

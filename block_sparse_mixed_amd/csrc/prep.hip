@@ -82,9 +82,11 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
 
     const uint64_t tileid = (uint64_t)bh * g.n_blocks + blk;
     if (tid == 0) a.ws[a.L.e8 + (uint64_t)tz * g.bh * g.n_blocks + tileid] = (uint8_t)(e8 + 127);
-    if (bh == 0 && tz == 0 && tid < DA2_TILE)   // geometry only: written once per block
-        reinterpret_cast<float*>(a.ws + a.L.bias)[(uint64_t)blk * DA2_TILE + tid] =
-            slot_raster(g, pos, tid) >= 0 ? 0.0f : -__builtin_huge_valf();
+    if (bh == 0 && tz == 0 && tid < DA2_TILE) {   // geometry only: written once per block
+        float* bias = reinterpret_cast<float*>(a.ws + a.L.bias);
+        bias[(uint64_t)blk * DA2_TILE + tid] = slot_raster(g, pos, tid) >= 0 ? 0.0f : -__builtin_huge_valf();
+        if (blk == 0) bias[(uint64_t)g.n_blocks * DA2_TILE + tid] = -__builtin_huge_valf();   // the empty tile
+    }
 
     if (tz < 2) {
         // ---- row pass (Q, K): E4M3 slot-major and MXFP4 along channels ----

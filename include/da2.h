@@ -101,7 +101,8 @@ typedef struct da2_plan_s da2_plan_t;
  *                               da2_set_labels
  *   status  u32 [4]             [0]: rows whose labels had the wrong counts
  *                               (written by da2_set_labels)
- *   bias    f32 [NB][T]         0 for a slot holding a token, -inf for a padded slot
+ *   bias    f32 [NB+1][T]       0 for a slot holding a token, -inf for a padded slot;
+ *                               row NB is all -inf (a key tile with no tokens)
  */
 typedef struct da2_plan_info_s {
     int32_t n_blocks;

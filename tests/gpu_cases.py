@@ -107,6 +107,13 @@ def check_prepare(run: GpuRun, bh: int, st: P.HeadState):
     G = st.ops["v4t_exp"].shape[-1]
     sv = run.sec("sv4t", torch.uint8, (BH, nb, T, 4))[bh].astype(int) - 127
     assert np.array_equal(sv[:, :d, :G], st.ops["v4t_exp"]), "v mxfp4 scales"
+    # key-slot bias: 0 for a token, -inf for a padded slot, and a last row for
+    # the empty key tile (every slot -inf)
+    bias = run.sec("bias", torch.float32, (nb + 1, T))
+    want_bias = np.full((nb + 1, T), -np.inf, dtype=np.float32)
+    for i in range(nb):
+        want_bias[i, :bs][st.valid[i]] = 0.0
+    assert np.array_equal(bias, want_bias), "key-slot bias"
     pool = run.sec("pool", torch.float64, (4, BH, nb, T))[:, bh, :, :d]
     np.testing.assert_allclose(pool[0], st.q_avg, rtol=1e-14, atol=1e-300)
     np.testing.assert_array_equal(pool[1], st.q_max)

@@ -105,7 +105,7 @@ def test_workspace_layout_is_aligned_and_disjoint():
              "e8": 3 * bh * nb, "q4": bh * nb * T * P // 2, "k4": bh * nb * T * P // 2, "v4t": bh * nb * P * T // 2,
              "sq4": bh * nb * T * 4, "sk4": bh * nb * T * 4, "sv4t": bh * nb * P * 4, "scores": 2 * bh * nb * nb * 8,
              "labels": bh * nb * nb, "hi": bh * nb * 50 * 4, "lo": bh * nb * 118 * 4, "status": 16,
-             "bias": nb * T * 4}
+             "bias": (nb + 1) * T * 4}
     spans = sorted((getattr(i, "off_" + k), getattr(i, "off_" + k) + v) for k, v in sizes.items())
     for (a0, a1), (b0, _) in zip(spans, spans[1:]):
         assert a1 <= b0
