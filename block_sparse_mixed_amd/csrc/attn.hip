@@ -301,20 +301,27 @@ struct QOps {
     int q4s[2];            // E8M0 scale of the lane's 32-channel group
 };
 
+// Every address below is a per-lane base plus a compile-time step offset
+// (the swizzles depend only on the lane), so the steps read through the LDS
+// instructions' immediate offsets.
 template <int PH>
 __device__ __forceinline__ void load_q(const WaveState& st, QOps& qo, int r, int g4) {
+    const int q0 = st.qs0 + r;                 // query slot of tile u = 0; u adds 16
+    if constexpr (PH == kHi) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int qs = st.qs0 + 16 * u + r;
-        if constexpr (PH == kHi) {
+        for (int kk = 0; kk < 4; ++kk) {
+            const uint8_t* qp = st.q + kQb + q0 * 256 + (((4 * g4 + kk) ^ (r & 7)) << 4);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                qo.qb[u][kk] = __builtin_bit_cast(
-                    v8bf, *reinterpret_cast<const uint4*>(st.q + kQb + qs * 256 + (((4 * g4 + kk) ^ (qs & 7)) << 4)));
-        } else {
-            const uint4 x = *reinterpret_cast<const uint4*>(st.q + kQ4 + qs * 64 + ((g4 ^ ((qs >> 1) & 3)) << 4));
-            qo.q4[u] = as_v4i(x);
-            qo.q4s[u] = st.q[kQs + qs * 4 + g4];
+            for (int u = 0; u < 2; ++u)
+                qo.qb[u][kk] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(qp + 4096 * u));
+        }
+    } else {
+        const uint8_t* qp = st.q + kQ4 + q0 * 64 + ((g4 ^ ((r >> 1) & 3)) << 4);
+        const uint8_t* sp = st.q + kQs + q0 * 4 + g4;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            qo.q4[u] = as_v4i(*reinterpret_cast<const uint4*>(qp + 1024 * u));
+            qo.q4s[u] = sp[64 * u];
         }
     }
 }
@@ -334,13 +341,16 @@ struct KLoOps {
 // widen them to bf16 in registers, exactly, just before the MFMAs. Lane
 // (r, g4) feeds channels 32 g4 + 8 kk .. + 7 as k-chunk kk; Q uses the same
 // assignment, which is all a bf16 MFMA requires of its operands.
+// slot_fp8(t, r) = slot_fp8(0, r) + 64 (t / 4) + 4 (t % 4), and its swizzle
+// depends on r only.
 __device__ __forceinline__ void load_k_hi(const uint8_t* ks, int t, int r, int g4, KHiOps& o) {
-    const int srow = slot_fp8(t, r);
-    const int sw = swz_k8f(srow);
+    const int srow0 = slot_fp8(0, r);
+    const int sw = swz_k8f(srow0);
+    const int step = 64 * (t >> 2) + 4 * (t & 3);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-        o.k[h] = *reinterpret_cast<const uint4*>(ks + srow * 128 + (((2 * g4 + h) ^ sw) << 4));
-    o.b = *reinterpret_cast<const v4f*>(ks + kKBias + 4 * slot_fp8(t, 4 * g4));
+        o.k[h] = *reinterpret_cast<const uint4*>(ks + srow0 * 128 + (((2 * g4 + h) ^ sw) << 4) + step * 128);
+    o.b = *reinterpret_cast<const v4f*>(ks + kKBias + 4 * slot_fp8(0, 4 * g4) + step * 4);
 }
 
 __device__ __forceinline__ v8bf widen_e4m3(uint32_t lo, uint32_t hi) {
@@ -351,12 +361,13 @@ __device__ __forceinline__ v8bf widen_e4m3(uint32_t lo, uint32_t hi) {
     return (v8bf){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// slot_fp4(t, r) = slot_fp4(0, r) + 4 t, and its swizzle depends on r only.
 __device__ __forceinline__ void load_k_lo(const uint8_t* ks, int t, int r, int g4, KLoOps& o) {
-    const int srow = slot_fp4(t, r);
-    const uint4 x = *reinterpret_cast<const uint4*>(ks + srow * 64 + ((g4 ^ swz_k4(srow)) << 4));
+    const int srow0 = slot_fp4(0, r);
+    const uint4 x = *reinterpret_cast<const uint4*>(ks + srow0 * 64 + ((g4 ^ swz_k4(srow0)) << 4) + t * 256);
     o.k = as_v4i(x);
-    o.sc = ks[kKScale + srow * 4 + g4];
-    o.b = *reinterpret_cast<const v4f*>(ks + kKBias + 4 * slot_fp4(t, 4 * g4));
+    o.sc = ks[kKScale + srow0 * 4 + g4 + t * 16];
+    o.b = *reinterpret_cast<const v4f*>(ks + kKBias + 4 * slot_fp4(0, 4 * g4) + t * 16);
 }
 
 // ---- S^T = K . Q^T for one key tile ----
@@ -427,11 +438,26 @@ __device__ __forceinline__ void scale_in_place(v4f& x, float f) {
     }
 }
 
+// Plain V_MAX3_F32 / V_MAX_F32: the scores are never NaN, so the NaN-quieting
+// moves that fmaxf adds in front of a maximum of MFMA results are not needed.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float vmax(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// The maximum of the lane's 32 scores: one chain of three-input maxima,
+// two new scores per instruction (the two query tiles' chains interleave).
 __device__ __forceinline__ float max32(const v4f (&s)[8]) {
-    float a = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+    float a = vmax3(s[0][0], s[0][1], s[0][2]);
 #pragma unroll
-    for (int t = 1; t < 8; ++t) a = fmaxf(fmaxf(a, s[t][0]), fmaxf(fmaxf(s[t][1], s[t][2]), s[t][3]));
-    return a;
+    for (int i = 3; i + 1 < 32; i += 2) a = vmax3(a, s[i >> 2][i & 3], s[(i + 1) >> 2][(i + 1) & 3]);
+    return vmax(a, s[7][3]);
 }
 
 // Max over the four lanes l, l^16, l^32, l^48. Each permlane swap exchanges
@@ -440,10 +466,10 @@ __device__ __forceinline__ float max32(const v4f (&s)[8]) {
 __device__ __forceinline__ float cross4max(float v) {
     const uint32_t u = __float_as_uint(v);
     const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const float m = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const uint32_t um = __float_as_uint(m);
     const auto b = __builtin_amdgcn_permlane16_swap(um, um, false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // ---- softmax of one tile: P operands and their E8M0 scales ----
@@ -542,16 +568,16 @@ struct VOps<kLo> {
 
 template <int PH>
 __device__ __forceinline__ void load_v(const uint8_t* vs, int ct, int r, int g4, int e_v, VOps<PH>& o) {
-    const int c = 16 * ct + r;
+    // channel c = 16 ct + r; its swizzle depends on r only
     if constexpr (PH == kHi) {
-        const int sw = swz_v8(c);
-        const uint4 x = *reinterpret_cast<const uint4*>(vs + c * 128 + ((g4 ^ sw) << 4));
-        const uint4 y = *reinterpret_cast<const uint4*>(vs + c * 128 + (((4 + g4) ^ sw) << 4));
+        const int sw = swz_v8(r);
+        const uint4 x = *reinterpret_cast<const uint4*>(vs + r * 128 + ((g4 ^ sw) << 4) + ct * 2048);
+        const uint4 y = *reinterpret_cast<const uint4*>(vs + r * 128 + (((4 + g4) ^ sw) << 4) + ct * 2048);
         o.v = (v8i){(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
         o.sc = e_v + 127;
     } else {
-        o.v = as_v4i(*reinterpret_cast<const uint4*>(vs + c * 64 + ((g4 ^ swz_v4(c)) << 4)));
-        o.sc = vs[kVScale + c * 4 + g4];
+        o.v = as_v4i(*reinterpret_cast<const uint4*>(vs + r * 64 + ((g4 ^ swz_v4(r)) << 4) + ct * 1024));
+        o.sc = vs[kVScale + r * 4 + g4 + ct * 64];
     }
 }
 
