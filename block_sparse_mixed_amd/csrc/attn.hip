@@ -675,41 +675,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
     const uint64_t qtile = (uint64_t)bh * nb + qb;
     const int n_tiles = g.n_hi + g.n_lo;
 
-    // this query block's tile list, packed with the fp8 exponents, into LDS
-    int32_t* tl = tlist;
-    {
-        const uint64_t plane = (uint64_t)g.bh * nb;
-        const int32_t* hl = reinterpret_cast<const int32_t*>(ws + a.L.hi) + qtile * g.n_hi;
-        const int32_t* ll = reinterpret_cast<const int32_t*>(ws + a.L.lo) + qtile * g.n_lo;
-        for (int i = tid; i < n_tiles; i += kThreads) {
-            uint32_t e;
-            if (i < g.n_hi) {
-                const int kb = hl[i];
-                const uint64_t kt = (uint64_t)bh * nb + kb;
-                e = (uint32_t)kb | ((uint32_t)ws[a.L.e8 + plane + kt] << 16) | ((uint32_t)ws[a.L.e8 + 2 * plane + kt] << 24);
-            } else {
-                e = (uint32_t)ll[i - g.n_hi];
-            }
-            tl[i] = (int32_t)e;
-        }
-    }
-    // The key and value slots start zeroed, so that every byte in them is a
-    // finite code or scale: the empty tile's PV reads value slots that no
-    // fetch has written yet (with P = 0).
-    {
-        const uint4 z = {0u, 0u, 0u, 0u};
-        for (int i = tid; i < kKSlot / 16; i += kThreads) {
-            reinterpret_cast<uint4*>(kslot0)[i] = z;
-            reinterpret_cast<uint4*>(kslot1)[i] = z;
-        }
-        for (int i = tid; i < kVSlot / 16; i += kThreads) {
-            reinterpret_cast<uint4*>(vslot0)[i] = z;
-            reinterpret_cast<uint4*>(vslot1)[i] = z;
-        }
-    }
-    __syncthreads();
-
-    // the query block's Q operands (swizzled rows)
+    // The query block's Q operands (swizzled rows) go first: their DMA runs
+    // while the tile list below is gathered.
     {
         const uint8_t* qb_src = ws + a.L.qb + qtile * (DA2_TILE * DA2_DPAD * 2);
 #pragma unroll
@@ -729,6 +696,53 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
         }
         if (w == 2 && lane < 32)
             dma16(ws + a.L.sq4 + qtile * (DA2_TILE * DA2_DPAD / 32) + lane * 16, qlds + kQs);
+    }
+
+    // This query block's tile list, packed with the fp8 exponents, into LDS.
+    // The head's K and V exponent rows are staged in the value slots first
+    // (coalesced loads), so that no list entry waits for a second global load.
+    int32_t* tl = tlist;
+    {
+        const uint64_t plane = (uint64_t)g.bh * nb;
+        uint8_t* ek_row = vslot0;
+        uint8_t* ev_row = vslot1;
+        for (int i = tid; i < nb; i += kThreads) {
+            ek_row[i] = ws[a.L.e8 + plane + (uint64_t)bh * nb + i];
+            ev_row[i] = ws[a.L.e8 + 2 * plane + (uint64_t)bh * nb + i];
+        }
+        const int32_t* hl = reinterpret_cast<const int32_t*>(ws + a.L.hi) + qtile * g.n_hi;
+        const int32_t* ll = reinterpret_cast<const int32_t*>(ws + a.L.lo) + qtile * g.n_lo;
+        int32_t mine[DA2_MAX_BLOCKS / kThreads];
+#pragma unroll
+        for (int k = 0; k < DA2_MAX_BLOCKS / kThreads; ++k) {
+            const int i = tid + k * kThreads;
+            mine[k] = i < g.n_hi ? hl[i] : (i < n_tiles ? ll[i - g.n_hi] : 0);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < DA2_MAX_BLOCKS / kThreads; ++k) {
+            const int i = tid + k * kThreads;
+            if (i < n_tiles) {
+                uint32_t e = (uint32_t)mine[k];
+                if (i < g.n_hi) e |= ((uint32_t)ek_row[e] << 16) | ((uint32_t)ev_row[e] << 24);
+                tl[i] = (int32_t)e;
+            }
+        }
+    }
+    __syncthreads();
+    // The key and value slots start zeroed, so that every byte in them is a
+    // finite code or scale: the empty tile's PV reads value slots that no
+    // fetch has written yet (with P = 0).
+    {
+        const uint4 z = {0u, 0u, 0u, 0u};
+        for (int i = tid; i < kKSlot / 16; i += kThreads) {
+            reinterpret_cast<uint4*>(kslot0)[i] = z;
+            reinterpret_cast<uint4*>(kslot1)[i] = z;
+        }
+        for (int i = tid; i < kVSlot / 16; i += kThreads) {
+            reinterpret_cast<uint4*>(vslot0)[i] = z;
+            reinterpret_cast<uint4*>(vslot1)[i] = z;
+        }
     }
 
     WaveState st;
