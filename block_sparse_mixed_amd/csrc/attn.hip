@@ -812,6 +812,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
         // phase p of the matrix team: PV(p-2) and QK^T(p); ev: entry of tile p-2
         auto mma_phase = [&](auto par, int p, int32_t ev) __attribute__((always_inline)) {
             constexpr int PAR = decltype(par)::value;
+            // In fp8 phases the matrix work is the longer: when both waves of
+            // a SIMD can issue, this one goes first (measured: 2 % faster;
+            // the same in MXFP4 phases, or for the softmax wave, is slower).
+            if constexpr (PH == kHi) __builtin_amdgcn_s_setprio(2);
             // the lane coordinates are recomputed here, not kept live
             const int ln = fresh_lane();
             const int r = ln & 15, g4 = ln >> 4;
@@ -820,6 +824,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
             load_q<PH>(st, qo, r, g4);
             pv<PH>(st, PAR ? vslot1 : vslot0, pop, psc, tile(p - 2, ev).e_v, r, g4);
             qk<PH>(PAR ? kslot1 : kslot0, qo, s, r, g4);
+            if constexpr (PH == kHi) __builtin_amdgcn_s_setprio(0);
         };
         // phase p of the other team: the softmax of tile p-1 (entry ek), with
         // the phase's fetch (fk, fv: entries of K(p+1) and V(p-1)) issued from
