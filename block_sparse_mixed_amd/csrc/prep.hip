@@ -50,8 +50,12 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
     __shared__ uint32_t red[kThreads / 64];
     __shared__ double psum[DA2_DPAD];
     __shared__ float pmax[DA2_DPAD];
+    __shared__ int sraster[DA2_TILE];          // raster index of each slot, -1 for padding
 
     const uint16_t* src = a.src[tz] + (int64_t)b * g.stride_b + (int64_t)h * g.stride_h;
+    // the window geometry once per slot (one integer division each), not per use
+    if (tid < DA2_TILE) sraster[tid] = (int)slot_raster(g, pos, tid);
+    __syncthreads();
 
     // ---- load: chunk ci = 8 channels of one slot; 16 chunks per slot row ----
     uint4 chunk[8];
@@ -61,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
         const int ci = tid + kThreads * it;
         const int s = ci >> 4;
         const int cc = ci & 15;
-        const int64_t n = slot_raster(g, pos, s);
+        const int64_t n = sraster[s];
         uint4 v = make_uint4(0, 0, 0, 0);
         if (n >= 0 && cc * 8 < g.head_dim) v = *reinterpret_cast<const uint4*>(src + n * g.stride_n + cc * 8);
         chunk[it] = v;
@@ -176,15 +180,22 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
             s4[grp] = (uint8_t)(e4 + 127);
         }
     } else {
-        // pooling over the real tokens: exact fp64 sums of bf16 values, signed max
-        double sum = 0.0;
-        float mx = -__builtin_huge_valf();
+        // pooling over the real tokens: fp64 sums of bf16 values, signed max.
+        // A bf16 value has 8 significant bits, so the sums are exact (and the
+        // four partial sums' order irrelevant) while a channel's values lie
+        // within 2^38 of each other. Padded slots hold zeros in the tile,
+        // which leave the sums unchanged; the max skips them.
+        double sum4[4] = {0.0, 0.0, 0.0, 0.0};
+        float mx4[4] = {-__builtin_huge_valf(), -__builtin_huge_valf(), -__builtin_huge_valf(),
+                        -__builtin_huge_valf()};
+#pragma unroll 4
         for (int s = half * 64; s < half * 64 + 64; ++s) {
-            if (slot_raster(g, pos, s) < 0) continue;
             const float x = bf16_bits_to_f32(tile[s * kPitch + c]);
-            sum += (double)x;
-            mx = fmaxf(mx, x);
+            sum4[s & 3] += (double)x;
+            mx4[s & 3] = sraster[s] >= 0 ? fmaxf(mx4[s & 3], x) : mx4[s & 3];
         }
+        double sum = (sum4[0] + sum4[1]) + (sum4[2] + sum4[3]);
+        float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
         if (half == 1) {
             psum[c] = sum;
             pmax[c] = mx;
