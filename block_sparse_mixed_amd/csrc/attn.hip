@@ -106,7 +106,6 @@ constexpr int kHi = 0, kLo = 1;
 // accumulators), which it doubles as; the tiles use at most 16 KiB of it.
 constexpr int kKBias = 32768, kKScale = 33280, kKSlot = 33792;
 constexpr int kVScale = 16384, kVSlot = 16896;
-constexpr int kSlots = 2;
 // Q: bf16 [128][256 B] | E2M1 [128][64 B] | E8M0 [128][4]
 constexpr int kQb = 0, kQ4 = 32768, kQs = 40960, kQBytes = 41472;
 constexpr int kListBytes = 4 * DA2_MAX_BLOCKS;    // packed tile list
@@ -177,12 +176,11 @@ __device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
 }
 
 struct Tile {
-    const uint8_t* k;      // bf16 K (fp8 tile) or E2M1 K
+    const uint8_t* k;      // E4M3 K (fp8 tile) or E2M1 K
     const uint8_t* v;      // E4M3 V^T or E2M1 V^T
     const uint8_t* ks;     // E2M1 K scales
     const uint8_t* vs;     // E2M1 V scales
     const float* bias;     // per-slot 0 / -inf
-    int hi;                // fp8 tile
     int e_k, e_v;          // fp8 block exponents
 };
 
@@ -199,7 +197,6 @@ __device__ __forceinline__ Tile tile_from(const AttnArgs& a, const uint8_t* __re
     const uint64_t kt = (uint64_t)bh * g.n_blocks + kb;
     Tile t;
     if constexpr (PH == kHi) {
-        t.hi = 1;
         t.k = ws + a.L.k8 + kt * (DA2_TILE * DA2_DPAD);
         t.v = ws + a.L.v8t + kt * (DA2_DPAD * DA2_TILE);
         t.ks = nullptr;
@@ -207,7 +204,6 @@ __device__ __forceinline__ Tile tile_from(const AttnArgs& a, const uint8_t* __re
         t.e_k = (int)((e >> 16) & 0xFFu) - 127;
         t.e_v = (int)(e >> 24) - 127;
     } else {
-        t.hi = 0;
         t.k = ws + a.L.k4 + kt * (DA2_TILE * DA2_DPAD / 2);
         t.v = ws + a.L.v4t + kt * (DA2_DPAD * DA2_TILE / 2);
         t.ks = ws + a.L.sk4 + kt * (DA2_TILE * 4);
@@ -227,49 +223,51 @@ __device__ __forceinline__ Tile tile_from(const AttnArgs& a, const uint8_t* __re
 template <int PH>
 constexpr int kFetchItems = PH == kHi ? 9 : 6;
 
+// Row wr (1 KiB) of a tile's K codes, or of its V^T codes, into a slot.
+template <int PH>
+__device__ __forceinline__ void k_row(const Tile& t, uint8_t* slot, int wr, const DmaOffsets& o) {
+    if constexpr (PH == kHi)   // 16 KiB of E4M3 K: 8 key rows per 1 KiB row
+        dma16(t.k + wr * 1024 + (o.k8f ^ (((wr >> 1) & 3) << 5)), slot + wr * 1024);
+    else                       // 8 KiB of E2M1 K
+        dma16(t.k + wr * 1024 + (o.k4 ^ ((wr & 2) << 4)), slot + wr * 1024);
+}
+template <int PH>
+__device__ __forceinline__ void v_row(const Tile& t, uint8_t* slot, int wr, const DmaOffsets& o) {
+    if constexpr (PH == kHi)   // 16 KiB of E4M3 V^T
+        dma16(t.v + wr * 1024 + o.v8, slot + wr * 1024);
+    else                       // 8 KiB of E2M1 V^T
+        dma16(t.v + wr * 1024 + o.v4, slot + wr * 1024);
+}
+// The key-slot bias (wave 0) and, for MXFP4 tiles, the K scales (wave 1).
+template <int PH>
+__device__ __forceinline__ void k_extras(const Tile& t, uint8_t* slot, int w, int lane) {
+    if constexpr (PH == kLo)
+        if (w == 1 && lane < 32) dma16(t.ks + lane * 16, slot + kKScale);
+    if (w == 0 && lane < 32) dma16(reinterpret_cast<const uint8_t*>(t.bias) + lane * 16, slot + kKBias);
+}
+
 template <int PH, int I>
-__device__ __forceinline__ void fetch_item(const Tile& tk, uint8_t* kslot, bool do_k, const Tile& tv, uint8_t* vslot,
-                                           bool do_v, int w, int lane, const DmaOffsets& o) {
+__device__ __forceinline__ void fetch_item(const Tile& tk, uint8_t* kslot, const Tile& tv, uint8_t* vslot, int w,
+                                           int lane, const DmaOffsets& o) {
     constexpr int kRows = (PH == kHi ? 16 : 8) / kTeamWaves;
     if constexpr (I < kRows) {
-        const int wr = w + kTeamWaves * I;
-        if (do_k) {
-            if constexpr (PH == kHi)   // 16 KiB of E4M3 K: 8 key rows per 1 KiB row
-                dma16(tk.k + wr * 1024 + (o.k8f ^ (((wr >> 1) & 3) << 5)), kslot + wr * 1024);
-            else                       // 8 KiB of E2M1 K
-                dma16(tk.k + wr * 1024 + (o.k4 ^ ((wr & 2) << 4)), kslot + wr * 1024);
-        }
+        k_row<PH>(tk, kslot, w + kTeamWaves * I, o);
     } else if constexpr (I < 2 * kRows) {
-        const int wr = w + kTeamWaves * (I - kRows);
-        if (do_v) {
-            if constexpr (PH == kHi)   // 16 KiB of E4M3 V^T
-                dma16(tv.v + wr * 1024 + o.v8, vslot + wr * 1024);
-            else                       // 8 KiB of E2M1 V^T
-                dma16(tv.v + wr * 1024 + o.v4, vslot + wr * 1024);
-        }
+        v_row<PH>(tv, vslot, w + kTeamWaves * (I - kRows), o);
     } else if constexpr (I == 2 * kRows) {
-        if (do_k) {
-            if constexpr (PH == kLo)
-                if (w == 1 && lane < 32) dma16(tk.ks + lane * 16, kslot + kKScale);
-            if (w == 0 && lane < 32) dma16(reinterpret_cast<const uint8_t*>(tk.bias) + lane * 16, kslot + kKBias);
-        }
+        k_extras<PH>(tk, kslot, w, lane);
     } else {
         static_assert(PH == kLo && I == 2 * kRows + 1, "fetch item");
-        if (do_v && w == 3 && lane < 32) dma16(tv.vs + lane * 16, vslot + kVScale);
+        if (w == 3 && lane < 32) dma16(tv.vs + lane * 16, vslot + kVScale);   // MXFP4 V scales
     }
 }
 
 // All of a team's K items of one tile (the first tile of a section).
 template <int PH>
 __device__ __forceinline__ void dma_k(const Tile& t, uint8_t* slot, int w, int lane, const DmaOffsets& o) {
-    auto all = [&](auto... is) __attribute__((always_inline)) {
-        (fetch_item<PH, decltype(is)::value>(t, slot, true, t, nullptr, false, w, lane, o), ...);
-    };
-    if constexpr (PH == kHi)
-        all(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{},
-            std::integral_constant<int, 3>{}, std::integral_constant<int, 8>{});
-    else
-        all(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 4>{});
+#pragma unroll
+    for (int n = 0; n < (PH == kHi ? 16 : 8) / kTeamWaves; ++n) k_row<PH>(t, slot, w + kTeamWaves * n, o);
+    k_extras<PH>(t, slot, w, lane);
 }
 
 struct WaveState {
@@ -841,7 +839,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
             uint8_t* vs = PAR ? vslot0 : vslot1;
             auto hook = [&](auto item) __attribute__((always_inline)) {
                 constexpr int I = decltype(item)::value;
-                if constexpr (I < kFetchItems<PH>) fetch_item<PH, I>(tk, ks, true, tv, vs, true, wq, ln, o);
+                if constexpr (I < kFetchItems<PH>) fetch_item<PH, I>(tk, ks, tv, vs, wq, ln, o);
             };
             softmax<PH>(st, s, tile(p - 1, ek).e_k, pop, psc, hook);
         };
