@@ -160,11 +160,16 @@ __global__ __launch_bounds__(256) void rank_kernel(Geo g, double* __restrict__ s
     }
     __syncthreads();
 
-    // bitonic sort, "a before b" iff C_a > C_b or (C_a == C_b and index_a < index_b)
+    // bitonic sort, "a before b" iff C_a > C_b or (C_a == C_b and index_a < index_b).
+    // Thread tid owns the compare pairs p = tid, tid + 256, ...; for a partner
+    // distance jj <= 64 the pairs of wave w touch only elements 128 w ..
+    // 128 w + 127 (and the same plus multiples of 512), so consecutive such
+    // steps need no workgroup barrier (a wave's LDS accesses complete in order).
     for (int k = 2; k <= np; k <<= 1) {
         for (int jj = k >> 1; jj > 0; jj >>= 1) {
+            const int lg = __builtin_ctz(jj);
             for (int p = tid; p < (np >> 1); p += 256) {
-                const int lo = (p / jj) * 2 * jj + (p % jj);
+                const int lo = ((p >> lg) << (lg + 1)) + (p & (jj - 1));
                 const int hi = lo + jj;
                 const double va = val[lo], vb = val[hi];
                 const int ia = idx[lo], ib = idx[hi];
@@ -178,9 +183,18 @@ __global__ __launch_bounds__(256) void rank_kernel(Geo g, double* __restrict__ s
                     idx[hi] = ia;
                 }
             }
-            __syncthreads();
+            // A workgroup barrier is needed when this step or the next one
+            // crosses waves (distance above 64); the next step's distance is
+            // jj / 2, or k when this stage ends. (With np > 512 a thread's
+            // second pair p + 256 lies 512 elements further, in the same
+            // wave's other chunk, which keeps small distances wave-local.)
+            if (jj > 64 || (jj == 1 && k > 64))
+                __syncthreads();
+            else
+                __builtin_amdgcn_wave_barrier();
         }
     }
+    __syncthreads();
     const int n_ret = g.n_hi + g.n_lo;
     for (int r = tid; r < nb; r += 256) lab[idx[r]] = (int8_t)(r < g.n_hi ? DA2_HI : (r < n_ret ? DA2_LO : DA2_SKIP));
     __syncthreads();
