@@ -76,6 +76,7 @@ namespace da2 {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
@@ -109,17 +110,23 @@ constexpr int kVScale = 16384, kVSlot = 16896;
 // Q: bf16 [128][256 B] | E2M1 [128][64 B] | E8M0 [128][4]
 constexpr int kQb = 0, kQ4 = 32768, kQs = 40960, kQBytes = 41472;
 constexpr int kListBytes = 4 * DA2_MAX_BLOCKS;    // packed tile list
-static_assert(2 * 66 * 64 * 4 <= kKSlot, "team merge area: two waves per K slot");
+static_assert(2 * 65 * 64 * 4 <= kKSlot, "team merge area: two waves per K slot");
 
 // LDS swizzles (16-byte chunk index XOR a row function) so that the eight
 // lanes served together by a 128-bit LDS read hit distinct banks.
-__device__ __forceinline__ int swz_k8f(int s) { return ((s >> 1) & 1) | (((s >> 4) & 3) << 1); }
+__device__ __forceinline__ int swz_k8f(int s) { return ((s >> 1) & 1) | (((s >> 4) & 1) << 1); }
 __device__ __forceinline__ int swz_v8(int c) { return c & 7; }
 __device__ __forceinline__ int swz_k4(int s) { return ((s >> 1) & 1) | ((s >> 4) & 2); }
 __device__ __forceinline__ int swz_v4(int c) { return (c >> 1) & 3; }
 
-__device__ __forceinline__ int slot_fp8(int t, int r) { return 64 * (t >> 2) + 16 * (r >> 2) + 4 * (t & 3) + (r & 3); }
-__device__ __forceinline__ int slot_fp4(int t, int r) { return 32 * (r >> 2) + 4 * t + (r & 3); }
+// The key slot fed to A row r (0 .. 31) of QK^T key block kb (0 .. 3). A
+// 32x32 MFMA result row r sits in lane half (r / 4) % 2 at register
+// 4 (r / 8) + r % 4; these maps make each lane's scores of one PV MFMA the
+// keys that the PV's V^T operand holds in natural slot order in that lane.
+__device__ __forceinline__ int sigma_fp8(int kb, int r) { return 32 * kb + 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+__device__ __forceinline__ int sigma_fp4(int kb, int r) {
+    return 64 * (kb >> 1) + 16 * (kb & 1) + 32 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+}
 
 // Keeps an MFMA source operand alive past its last MFMA, so that the register
 // allocator never gives that MFMA a destination overlapping the operand (the
@@ -170,7 +177,7 @@ __device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
     o.k4 = ((lane >> 2) << 6) + (((lane & 3) ^ ((lane >> 3) & 1)) << 4);
     o.v4 = ((lane >> 2) << 6) + (((lane & 3) ^ ((lane >> 3) & 3)) << 4);
     // E4M3 K rows (128 B): chunk c of row s sits at c ^ swz_k8f(s); a DMA of
-    // rows 8i .. 8i+7 gathers with this offset XOR (((i >> 1) & 3) << 5)
+    // rows 8i .. 8i+7 gathers with this offset XOR (((i >> 1) & 1) << 5)
     o.k8f = ((lane >> 3) << 7) + (((lane & 7) ^ ((lane >> 4) & 1)) << 4);
     return o;
 }
@@ -227,7 +234,7 @@ constexpr int kFetchItems = PH == kHi ? 9 : 6;
 template <int PH>
 __device__ __forceinline__ void k_row(const Tile& t, uint8_t* slot, int wr, const DmaOffsets& o) {
     if constexpr (PH == kHi)   // 16 KiB of E4M3 K: 8 key rows per 1 KiB row
-        dma16(t.k + wr * 1024 + (o.k8f ^ (((wr >> 1) & 3) << 5)), slot + wr * 1024);
+        dma16(t.k + wr * 1024 + (o.k8f ^ (((wr >> 1) & 1) << 5)), slot + wr * 1024);
     else                       // 8 KiB of E2M1 K
         dma16(t.k + wr * 1024 + (o.k4 ^ ((wr & 2) << 4)), slot + wr * 1024);
 }
@@ -273,15 +280,17 @@ __device__ __forceinline__ void dma_k(const Tile& t, uint8_t* slot, int w, int l
 struct WaveState {
     const uint8_t* q;      // LDS Q block
     int qs0;               // first query slot of this wave
-    v4f acc[2][8];         // O^T: [u][channel tile]; lane holds channels 16ct + 4g + e of query r
-    v4f lsum[2];           // row sums (all four elements equal)
-    float m[2];            // running integer max (log2 units)
-    float mref[2];         // acc and lsum hold values relative to 2^mref
+    // O^T by channel block cb: element j holds channel 32 cb + 8 (j / 4) + 4 h
+    // + j % 4 of the lane's query (h = lane / 32)
+    v16f acc[4];
+    v16f lsum;             // the query's row sum (all sixteen elements equal)
+    float m;               // running integer max (log2 units)
+    float mref;            // acc and lsum hold values relative to 2^mref
     float c_lo;            // tau * log2(e)
     float c_hi_q;          // tau * log2(e) * 2^e_q8
 };
 
-// A 16x16x128 MFMA operand in E2M1 occupies four registers; the builtin takes
+// A 32x32x64 MFMA operand in E2M1 occupies four registers; the builtin takes
 // eight, of which the hardware reads the first four for this format. Building
 // the vector at the call keeps only the four live values in registers.
 __device__ __forceinline__ v8i fp4_operand(v4i x) {
@@ -290,65 +299,36 @@ __device__ __forceinline__ v8i fp4_operand(v4i x) {
 
 __device__ __forceinline__ v4i as_v4i(const uint4& x) { return (v4i){(int)x.x, (int)x.y, (int)x.z, (int)x.w}; }
 
-// ---- Q operands of the wave's two query tiles, read from LDS ----
+// ---- Q operands of the wave's 32 queries, read from LDS ----
 // Q rows in LDS are swizzled like the K rows: bf16 16-byte chunk c of query
 // slot q sits at chunk c ^ (q & 7); E2M1 chunk c at c ^ ((q >> 1) & 3).
+// Lane (query q, half h) feeds the bf16 MFMAs channels 32 i + 16 h .. + 15
+// (two MFMAs of 8 channels per i) and the E2M1 MFMAs channels 64 c + 32 h ..
+// + 31; K uses the same assignment.
 struct QOps {
-    v8bf qb[2][4];         // bf16 (fp8 phase): [u][k-chunk]
-    v4i q4[2];             // E2M1 (MXFP4 phase)
-    int q4s[2];            // E8M0 scale of the lane's 32-channel group
+    v8bf qb[4][2];         // bf16 (fp8 phase): [i][e], channels 32 i + 16 h + 8 e .. + 7
+    v4i q4[2];             // E2M1 (MXFP4 phase): [c], channels 64 c + 32 h .. + 31
+    int q4s[2];            // their E8M0 scales
 };
 
-// Every address below is a per-lane base plus a compile-time step offset
-// (the swizzles depend only on the lane), so the steps read through the LDS
-// instructions' immediate offsets.
 template <int PH>
-__device__ __forceinline__ void load_q(const WaveState& st, QOps& qo, int r, int g4) {
-    const int q0 = st.qs0 + r;                 // query slot of tile u = 0; u adds 16
+__device__ __forceinline__ void load_q(const WaveState& st, QOps& qo, int q, int h) {
+    const int qs = st.qs0 + q;                 // qs & 7 == q & 7: qs0 is a multiple of 32
     if constexpr (PH == kHi) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const uint8_t* qp = st.q + kQb + q0 * 256 + (((4 * g4 + kk) ^ (r & 7)) << 4);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-                qo.qb[u][kk] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(qp + 4096 * u));
-        }
+            for (int e = 0; e < 2; ++e)
+                qo.qb[i][e] = __builtin_bit_cast(
+                    v8bf, *reinterpret_cast<const uint4*>(st.q + kQb + qs * 256 + (((4 * i + 2 * h + e) ^ (q & 7)) << 4)));
     } else {
-        const uint8_t* qp = st.q + kQ4 + q0 * 64 + ((g4 ^ ((r >> 1) & 3)) << 4);
-        const uint8_t* sp = st.q + kQs + q0 * 4 + g4;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            qo.q4[u] = as_v4i(*reinterpret_cast<const uint4*>(qp + 1024 * u));
-            qo.q4s[u] = sp[64 * u];
+        for (int c = 0; c < 2; ++c) {
+            const int chunk = 2 * c + h;
+            qo.q4[c] = as_v4i(*reinterpret_cast<const uint4*>(st.q + kQ4 + qs * 64 + ((chunk ^ ((q >> 1) & 3)) << 4)));
+            qo.q4s[c] = st.q[kQs + qs * 4 + chunk];
         }
     }
-}
-
-// Operands of one 16-key step t of a key tile.
-struct KHiOps {
-    uint4 k[2];            // 32 E4M3 codes: channels 32 g4 .. 32 g4 + 31
-    v4f b;                 // bias of the lane's four keys (0 or -inf)
-};
-struct KLoOps {
-    v4i k;
-    v4f b;
-    int sc;
-};
-
-// The fp8 tiles keep K as E4M3 codes in LDS (half the bytes of bf16) and
-// widen them to bf16 in registers, exactly, just before the MFMAs. Lane
-// (r, g4) feeds channels 32 g4 + 8 kk .. + 7 as k-chunk kk; Q uses the same
-// assignment, which is all a bf16 MFMA requires of its operands.
-// slot_fp8(t, r) = slot_fp8(0, r) + 64 (t / 4) + 4 (t % 4), and its swizzle
-// depends on r only.
-__device__ __forceinline__ void load_k_hi(const uint8_t* ks, int t, int r, int g4, KHiOps& o) {
-    const int srow0 = slot_fp8(0, r);
-    const int sw = swz_k8f(srow0);
-    const int step = 64 * (t >> 2) + 4 * (t & 3);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-        o.k[h] = *reinterpret_cast<const uint4*>(ks + srow0 * 128 + (((2 * g4 + h) ^ sw) << 4) + step * 128);
-    o.b = *reinterpret_cast<const v4f*>(ks + kKBias + 4 * slot_fp8(0, 4 * g4) + step * 4);
 }
 
 __device__ __forceinline__ v8bf widen_e4m3(uint32_t lo, uint32_t hi) {
@@ -359,63 +339,94 @@ __device__ __forceinline__ v8bf widen_e4m3(uint32_t lo, uint32_t hi) {
     return (v8bf){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// slot_fp4(t, r) = slot_fp4(0, r) + 4 t, and its swizzle depends on r only.
-__device__ __forceinline__ void load_k_lo(const uint8_t* ks, int t, int r, int g4, KLoOps& o) {
-    const int srow0 = slot_fp4(0, r);
-    const uint4 x = *reinterpret_cast<const uint4*>(ks + srow0 * 64 + ((g4 ^ swz_k4(srow0)) << 4) + t * 256);
-    o.k = as_v4i(x);
-    o.sc = ks[kKScale + srow0 * 4 + g4 + t * 16];
-    o.b = *reinterpret_cast<const v4f*>(ks + kKBias + 4 * slot_fp4(0, 4 * g4) + t * 16);
-}
-
 // ---- S^T = K . Q^T for one key tile ----
-// The LDS reads of step t + D are issued before the MFMAs of step t (D = 1
-// for the fp8 phase, whose steps are eight MFMAs long; D = 2 for MXFP4, two
-// MFMAs per step), so the MFMA pipe does not wait for LDS latency.
+// Output s[kb] (key block kb of 32 rows): element j of lane (q, h) is the
+// score of query q against the key slot the row 8 (j / 4) + 4 h + j % 4 of
+// block kb was fed with, which is slot 32 kb + 16 h + j (fp8) or
+// 64 (kb / 2) + 32 h + 16 (kb % 2) + j (MXFP4): see sigma_fp8 / sigma_fp4.
+// The accumulator starts at the key's bias (0, or -inf for a padded slot).
 template <int PH>
-__device__ __forceinline__ void qk(const uint8_t* ks, QOps& qo, v4f (&s)[2][8], int r, int g4) {
+__device__ __forceinline__ void qk(const uint8_t* ks, QOps& qo, v16f (&s)[4], int q, int h) {
     if constexpr (PH == kHi) {
-        KHiOps o[2];
-        load_k_hi(ks, 0, r, g4, o[0]);
+        // A row q of block kb is key slot sigma_fp8(kb, q) = 32 kb + rho(q);
+        // the swizzle of that row depends on q only
+        const int rho = sigma_fp8(0, q);
+        const int sw = swz_k8f(rho);
+        // lane base addresses of the 16-byte chunks 2 i + h, i = 0 .. 3
+        const uint8_t* kp[4];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            if (t + 1 < 8) load_k_hi(ks, t + 1, r, g4, o[(t + 1) & 1]);
-            KHiOps& c = o[t & 1];
-            v8bf kb[4];
+        for (int i = 0; i < 4; ++i) kp[i] = ks + rho * 128 + (((2 * i + h) ^ sw) << 4);
+        const uint8_t* bp = ks + kKBias + 64 * h;
+        // one step = (kb, i): 16 E4M3 codes, widened, feed two MFMAs; the
+        // codes of the next step are read first
+        uint4 code[2];
+        code[0] = *reinterpret_cast<const uint4*>(kp[0]);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const uint4& x = c.k[kk >> 1];
-                kb[kk] = (kk & 1) ? widen_e4m3(x.z, x.w) : widen_e4m3(x.x, x.y);
+        for (int kb = 0; kb < 4; ++kb) {
+            v16f d;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const v4f b4 = *reinterpret_cast<const v4f*>(bp + 128 * kb + 16 * e4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) d[4 * e4 + e] = b4[e];
             }
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                v4f d = c.b;
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qo.qb[u][kk], d, 0, 0, 0);
-                s[u][t] = d;
+            for (int i = 0; i < 4; ++i) {
+                const int step = 4 * kb + i;
+                if (step + 1 < 16)
+                    code[(step + 1) & 1] =
+                        *reinterpret_cast<const uint4*>(kp[(step + 1) & 3] + 4096 * ((step + 1) >> 2));
+                const uint4& x = code[step & 1];
+                v8bf kb0 = widen_e4m3(x.x, x.y);
+                v8bf kb1 = widen_e4m3(x.z, x.w);
+                d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb0, qo.qb[i][0], d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb1, qo.qb[i][1], d, 0, 0, 0);
+                keep(kb0);
+                keep(kb1);
+                fence();
             }
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) keep(kb[kk]);
-            fence();
+            s[kb] = d;
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) keep(qo.qb[u][kk]);
+        for (int i = 0; i < 4; ++i) {
+            keep(qo.qb[i][0]);
+            keep(qo.qb[i][1]);
+        }
     } else {
-        constexpr int D = 2;
-        KLoOps o[D + 1];
+        const int rho = sigma_fp4(0, q);           // sigma_fp4(kb, q) = rho + 64 (kb / 2) + 16 (kb % 2)
+        const int sw = swz_k4(rho);
+        const uint8_t* kp[2];
+        const uint8_t* sp[2];
 #pragma unroll
-        for (int t = 0; t < D; ++t) load_k_lo(ks, t, r, g4, o[t]);
+        for (int c = 0; c < 2; ++c) {
+            kp[c] = ks + rho * 64 + (((2 * c + h) ^ sw) << 4);
+            sp[c] = ks + kKScale + rho * 4 + 2 * c + h;
+        }
+        const uint8_t* bp = ks + kKBias + 128 * h;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            if (t + D < 8) load_k_lo(ks, t + D, r, g4, o[(t + D) % (D + 1)]);
-            KLoOps& c = o[t % (D + 1)];
+        for (int kb = 0; kb < 4; ++kb) {
+            const int off = 64 * (kb >> 1) + 16 * (kb & 1);     // slot offset of block kb's rows
+            v16f d;
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-                s[u][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(c.k), fp4_operand(qo.q4[u]), c.b, kFmtFp4,
-                                                                          kFmtFp4, 0, c.sc, 0, qo.q4s[u]);
-            keep(c.k);
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const v4f b4 = *reinterpret_cast<const v4f*>(bp + 4 * off + 16 * e4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) d[4 * e4 + e] = b4[e];
+            }
+            v4i k4[2];
+            int ksc[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                k4[c] = as_v4i(*reinterpret_cast<const uint4*>(kp[c] + off * 64));
+                ksc[c] = sp[c][off * 4];
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(k4[c]), fp4_operand(qo.q4[c]), d, kFmtFp4,
+                                                                   kFmtFp4, 0, ksc[c], 0, qo.q4s[c]);
+            keep(k4[0]);
+            keep(k4[1]);
+            s[kb] = d;
             fence();
         }
         keep(qo.q4[0]);
@@ -427,9 +438,9 @@ __device__ __forceinline__ void qk(const uint8_t* ks, QOps& qo, v4f (&s)[2][8], 
 // branch lets the register allocator place the product elsewhere, and the
 // merge after the branch then costs a copy of the whole accumulator on the
 // common path.
-__device__ __forceinline__ void scale_in_place(v4f& x, float f) {
+__device__ __forceinline__ void scale_in_place(v16f& x, float f) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 16; ++e) {
         float y = x[e];
         asm("v_mul_f32 %0, %0, %1" : "+v"(y) : "v"(f));
         x[e] = y;
@@ -449,25 +460,21 @@ __device__ __forceinline__ float vmax(float a, float b) {
     return r;
 }
 
-// The maximum of the lane's 32 scores: one chain of three-input maxima,
-// two new scores per instruction (the two query tiles' chains interleave).
-__device__ __forceinline__ float max32(const v4f (&s)[8]) {
-    float a = vmax3(s[0][0], s[0][1], s[0][2]);
+// The maximum of 32 scores (two key blocks): one chain of three-input maxima.
+__device__ __forceinline__ float max32(const v16f& x, const v16f& y) {
+    float a = vmax3(x[0], x[1], x[2]);
 #pragma unroll
-    for (int i = 3; i + 1 < 32; i += 2) a = vmax3(a, s[i >> 2][i & 3], s[(i + 1) >> 2][(i + 1) & 3]);
-    return vmax(a, s[7][3]);
+    for (int i = 3; i + 1 < 32; i += 2) a = vmax3(a, i < 16 ? x[i] : y[i - 16], i + 1 < 16 ? x[i + 1] : y[i - 15]);
+    return vmax(a, y[15]);
 }
 
-// Max over the four lanes l, l^16, l^32, l^48. Each permlane swap exchanges
-// two halves of a copy of v with each other, so the maximum of its two
-// results is the pairwise maximum whichever half moves where; no LDS traffic.
-__device__ __forceinline__ float cross4max(float v) {
+// Max over the two lanes l and l ^ 32 (the query's two halves of keys): the
+// permlane swap exchanges two copies' halves, so the maximum of its two
+// results is the pairwise maximum; no LDS traffic.
+__device__ __forceinline__ float cross2max(float v) {
     const uint32_t u = __float_as_uint(v);
     const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    const float m = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const uint32_t um = __float_as_uint(m);
-    const auto b = __builtin_amdgcn_permlane16_swap(um, um, false, false);
-    return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
 }
 
 // ---- softmax of one tile: P operands and their E8M0 scales ----
@@ -479,84 +486,83 @@ __device__ __forceinline__ float cross4max(float v) {
 // the accumulator. Only when m runs more than kMaxLead above mref (or at the
 // first tile, mref = -inf) is the accumulator rescaled, by an exact power of
 // two, and mref moved to m.
+//   P operand of PV MFMA n (keys 64 n .. 64 n + 63 of the PV order): the
+// lane's scores of key blocks 2 n and 2 n + 1, in register order.
 constexpr float kMaxLead = 64.0f;
 
-// hook(i) issues fetch item i of the phase (nothing for i past the last):
-// the items are spread through the softmax so that each DMA instruction's
-// hold on this wave is interleaved with the wave's own arithmetic.
 template <int PH, class Hook>
-__device__ __forceinline__ void softmax(WaveState& st, const v4f (&s)[2][8], int e_k, v8i (&pop)[2], int (&psc)[2],
+__device__ __forceinline__ void softmax(WaveState& st, const v16f (&s)[4], int e_k, v8i (&pop)[2], int (&psc)[2],
                                         Hook&& hook) {
     const float cs = PH == kHi ? ldexpf(st.c_hi_q, e_k) : st.c_lo;
-    float gmax[2], mnew[2];
+    float gmax[2];                                       // per PV MFMA n: the lane's 32 raw scores
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        gmax[u] = max32(s[u]);                           // this lane's 32 keys (raw scores)
-        mnew[u] = fmaxf(st.m[u], ceilf(cross4max(gmax[u]) * cs));
-    }
+    for (int n = 0; n < 2; ++n) gmax[n] = max32(s[2 * n], s[2 * n + 1]);
+    const float mnew = fmaxf(st.m, ceilf(cross2max(vmax(gmax[0], gmax[1])) * cs));
     hook(std::integral_constant<int, 0>{});
-    if (!(st.mref[0] >= mnew[0] - kMaxLead) || !(st.mref[1] >= mnew[1] - kMaxLead)) {
+    if (!(st.mref >= mnew - kMaxLead)) {
+        const float f = exp2f(st.mref - mnew);           // 0 while mref = -inf
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const float f = exp2f(st.mref[u] - mnew[u]);  // 0 while mref = -inf
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct) scale_in_place(st.acc[u][ct], f);
-            scale_in_place(st.lsum[u], f);
-            st.mref[u] = mnew[u];
-        }
+        for (int cb = 0; cb < 4; ++cb) scale_in_place(st.acc[cb], f);
+        scale_in_place(st.lsum, f);
+        st.mref = mnew;
     }
-    static_for<2>([&](auto uc) __attribute__((always_inline)) {
-        constexpr int U = decltype(uc)::value;
-        constexpr int u = U;
+    static_for<2>([&](auto nc) __attribute__((always_inline)) {
+        constexpr int n = decltype(nc)::value;
         if constexpr (PH == kHi) {
             // finite also while no key has been seen (mnew = -inf): the
             // scores are then -inf and the codes 0
-            const float off = 8.0f - fmaxf(mnew[u], -__FLT_MAX__);
-            static_for<8>([&](auto tc) __attribute__((always_inline)) {
-                constexpr int t = decltype(tc)::value;
-                pop[u][t] = (int)pack_fp8x4(__builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][0], cs, off)),
-                                            __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][1], cs, off)),
-                                            __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][2], cs, off)),
-                                            __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][3], cs, off)));
-                if constexpr ((t & 1) == 1) {
-                    hook(std::integral_constant<int, 1 + 4 * U + (t >> 1)>{});
+            const float off = 8.0f - fmaxf(mnew, -__FLT_MAX__);
+            static_for<8>([&](auto dc) __attribute__((always_inline)) {
+                constexpr int d = decltype(dc)::value;   // bytes 4 d .. 4 d + 3
+                const v16f& x = s[2 * n + (d >> 2)];
+                constexpr int j = 4 * (d & 3);
+                pop[n][d] = (int)pack_fp8x4(__builtin_amdgcn_exp2f(__builtin_fmaf(x[j], cs, off)),
+                                            __builtin_amdgcn_exp2f(__builtin_fmaf(x[j + 1], cs, off)),
+                                            __builtin_amdgcn_exp2f(__builtin_fmaf(x[j + 2], cs, off)),
+                                            __builtin_amdgcn_exp2f(__builtin_fmaf(x[j + 3], cs, off)));
+                if constexpr ((d & 1) == 1) {
+                    hook(std::integral_constant<int, 1 + 4 * n + (d >> 1)>{});
                     fence();
                 }
             });
             // 127 .. 127 + kMaxLead (127 while no key has been seen: both -inf)
-            psc[u] = 127 + (int)fmaxf(mnew[u] - st.mref[u], 0.0f);
+            psc[n] = 127 + (int)fmaxf(mnew - st.mref, 0.0f);
         } else {
-            // MX group of P = this lane's 32 keys: scale 2^F, F the smallest
-            // integer with 2^(gmax cs) <= 6 * 2^F; codes RNE(2^(x - F)).
-            const bool any = gmax[u] > -__builtin_huge_valf();
-            const float F = any ? ceilf(gmax[u] * cs - kLog2Six) : 0.0f;
+            // MX group of P = the lane's 32 keys of this PV MFMA: scale 2^F,
+            // F the smallest integer with 2^(gmax cs) <= 6 * 2^F; codes
+            // RNE(2^(x - F)).
+            const bool any = gmax[n] > -__builtin_huge_valf();
+            const float F = any ? ceilf(gmax[n] * cs - kLog2Six) : 0.0f;
             const float off = -F;
             static_for<4>([&](auto dc) __attribute__((always_inline)) {
-                constexpr int d = decltype(dc)::value;
+                constexpr int d = decltype(dc)::value;   // nibbles 8 d .. 8 d + 7
+                const v16f& x = s[2 * n + (d >> 1)];
+                constexpr int j = 8 * (d & 1);
                 float v[8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    v[q] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][2 * d + (q >> 2)][q & 3], cs, off));
-                pop[u][d] = (int)pack_fp4x8(v);
-                hook(std::integral_constant<int, 1 + 4 * U + d>{});
+                for (int e = 0; e < 8; ++e) v[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j + e], cs, off));
+                pop[n][d] = (int)pack_fp4x8(v);
+                hook(std::integral_constant<int, 1 + 4 * n + d>{});
                 fence();
             });
-            const int sc = any ? (int)(F - st.mref[u]) + 8 + 127 : 0;
-            psc[u] = min(254, max(0, sc));
+            const int sc = any ? (int)(F - st.mref) + 8 + 127 : 0;
+            psc[n] = min(254, max(0, sc));
         }
     });
-    st.m[0] = mnew[0];
-    st.m[1] = mnew[1];
+    st.m = mnew;
 }
 
 // ---- O^T += V^T . P^T and l += 1 . P^T ----
-// V^T operands of channel tile ct are read three tiles ahead of their MFMAs.
+// PV MFMA (n, cb): A = V^T channels 32 cb .. + 31 over keys 64 n .. + 63 in
+// natural slot order. Lane (channel row q, half h) holds, for fp8, the 16
+// slots 64 n + 16 h .. + 15 then 64 n + 32 + 16 h .. + 15, and for E2M1 the
+// 32 slots 64 n + 32 h .. + 31: exactly the keys whose P the lane of query q
+// and the same half holds (see qk).
 template <int PH>
 struct VOps;
 template <>
 struct VOps<kHi> {
     v8i v;                 // E4M3
-    int sc;
 };
 template <>
 struct VOps<kLo> {
@@ -565,50 +571,55 @@ struct VOps<kLo> {
 };
 
 template <int PH>
-__device__ __forceinline__ void load_v(const uint8_t* vs, int ct, int r, int g4, int e_v, VOps<PH>& o) {
-    // channel c = 16 ct + r; its swizzle depends on r only
+__device__ __forceinline__ void load_v(const uint8_t* vs, int n, int cb, int q, int h, VOps<PH>& o) {
+    // channel 32 cb + q; its swizzle depends on q only
     if constexpr (PH == kHi) {
-        const int sw = swz_v8(r);
-        const uint4 x = *reinterpret_cast<const uint4*>(vs + r * 128 + ((g4 ^ sw) << 4) + ct * 2048);
-        const uint4 y = *reinterpret_cast<const uint4*>(vs + r * 128 + (((4 + g4) ^ sw) << 4) + ct * 2048);
+        const int sw = swz_v8(q);
+        const uint8_t* row = vs + (32 * cb + q) * 128;
+        const uint4 x = *reinterpret_cast<const uint4*>(row + (((4 * n + h) ^ sw) << 4));
+        const uint4 y = *reinterpret_cast<const uint4*>(row + (((4 * n + 2 + h) ^ sw) << 4));
         o.v = (v8i){(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-        o.sc = e_v + 127;
     } else {
-        o.v = as_v4i(*reinterpret_cast<const uint4*>(vs + r * 64 + ((g4 ^ swz_v4(r)) << 4) + ct * 1024));
-        o.sc = vs[kVScale + r * 4 + g4 + ct * 64];
+        const uint8_t* row = vs + (32 * cb + q) * 64;
+        o.v = as_v4i(*reinterpret_cast<const uint4*>(row + (((2 * n + h) ^ swz_v4(q)) << 4)));
+        o.sc = vs[kVScale + (32 * cb + q) * 4 + 2 * n + h];
     }
 }
 
 template <int PH>
 __device__ __forceinline__ void pv(WaveState& st, const uint8_t* vs, v8i (&pop)[2], const int (&psc)[2], int e_v,
-                                   int r, int g4) {
+                                   int q, int h) {
     constexpr int fmt = PH == kHi ? kFmtFp8 : kFmtFp4;
-    constexpr int D = 3;
+    constexpr int D = 2;
     VOps<PH> o[D + 1];
-    // B operand: P^T of the two query tiles (E2M1 uses the low four dwords)
+    // B operand: P^T (E2M1 uses the low four dwords)
     v8i pb[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int n = 0; n < 2; ++n) {
         if constexpr (PH == kHi)
-            pb[u] = pop[u];
+            pb[n] = pop[n];
         else
-            pb[u] = fp4_operand(__builtin_shufflevector(pop[u], pop[u], 0, 1, 2, 3));
+            pb[n] = fp4_operand(__builtin_shufflevector(pop[n], pop[n], 0, 1, 2, 3));
     }
+    const int vsc_hi = e_v + 127;
+    // steps (n, cb), V^T operands read D steps ahead
 #pragma unroll
-    for (int ct = 0; ct < D; ++ct) load_v<PH>(vs, ct, r, g4, e_v, o[ct]);
+    for (int t = 0; t < D; ++t) load_v<PH>(vs, t >> 2, t & 3, q, h, o[t]);
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-        if (ct + D < 8) load_v<PH>(vs, ct + D, r, g4, e_v, o[(ct + D) % (D + 1)]);
-        VOps<PH>& c = o[ct % (D + 1)];
+    for (int t = 0; t < 8; ++t) {
+        if (t + D < 8) load_v<PH>(vs, (t + D) >> 2, (t + D) & 3, q, h, o[(t + D) % (D + 1)]);
+        VOps<PH>& c = o[t % (D + 1)];
+        const int n = t >> 2, cb = t & 3;
         v8i va;
-        if constexpr (PH == kHi)
+        int vsc;
+        if constexpr (PH == kHi) {
             va = c.v;
-        else
+            vsc = vsc_hi;
+        } else {
             va = fp4_operand(c.v);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            st.acc[u][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, pb[u], st.acc[u][ct], fmt, fmt, 0, c.sc, 0,
-                                                                             psc[u]);
+            vsc = c.sc;
+        }
+        st.acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb[n], st.acc[cb], fmt, fmt, 0, vsc, 0, psc[n]);
         keep(c.v);
         fence();
     }
@@ -618,10 +629,10 @@ __device__ __forceinline__ void pv(WaveState& st, const uint8_t* vs, v8i (&pop)[
     asm volatile("" : "+v"(one));          // not hoisted out of the loop
     v8i ones;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) ones[q] = (PH == kHi || q < 4) ? one : 0;
+    for (int w = 0; w < 8; ++w) ones[w] = (PH == kHi || w < 4) ? one : 0;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-        st.lsum[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pb[u], st.lsum[u], fmt, fmt, 0, 127, 0, psc[u]);
+    for (int n = 0; n < 2; ++n)
+        st.lsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb[n], st.lsum, fmt, fmt, 0, 127, 0, psc[n]);
     keep(one);
     if constexpr (PH == kHi) {
         keep(pop[0]);
@@ -746,13 +757,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
     WaveState st;
     st.q = qlds;
     st.qs0 = 32 * wq;
+    st.m = -__builtin_huge_valf();
+    st.mref = -__builtin_huge_valf();
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        st.m[u] = -__builtin_huge_valf();
-        st.mref[u] = -__builtin_huge_valf();
-        st.lsum[u] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 16; ++e) {
+        st.lsum[e] = 0.f;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) st.acc[u][ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+        for (int cb = 0; cb < 4; ++cb) st.acc[cb][e] = 0.f;
     }
     st.c_lo = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, (float)g.tau * kLog2E)));
     {
@@ -763,7 +774,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    v4f s[2][8];
+    v16f s[4];
     v8i pop[2];
     int psc[2];
 
@@ -816,12 +827,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
             if constexpr (PH == kHi) __builtin_amdgcn_s_setprio(2);
             // the lane coordinates are recomputed here, not kept live
             const int ln = fresh_lane();
-            const int r = ln & 15, g4 = ln >> 4;
+            const int q = ln & 31, h = ln >> 5;
             // Q operands for this phase's QK^T are read first, under the PV
             QOps qo;
-            load_q<PH>(st, qo, r, g4);
-            pv<PH>(st, PAR ? vslot1 : vslot0, pop, psc, tile(p - 2, ev).e_v, r, g4);
-            qk<PH>(PAR ? kslot1 : kslot0, qo, s, r, g4);
+            load_q<PH>(st, qo, q, h);
+            pv<PH>(st, PAR ? vslot1 : vslot0, pop, psc, tile(p - 2, ev).e_v, q, h);
+            qk<PH>(PAR ? kslot1 : kslot0, qo, s, q, h);
             if constexpr (PH == kHi) __builtin_amdgcn_s_setprio(0);
         };
         // phase p of the other team: the softmax of tile p-1 (entry ek), with
@@ -858,15 +869,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
         }
         // before the section: the scores of the empty tile, no P
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            psc[u] = 127;
+        for (int n = 0; n < 2; ++n) {
+            psc[n] = 127;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) pop[u][q] = 0;
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-                s[u][t] = (v4f){-__builtin_huge_valf(), -__builtin_huge_valf(), -__builtin_huge_valf(),
-                                -__builtin_huge_valf()};
+            for (int w = 0; w < 8; ++w) pop[n][w] = 0;
         }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[kb][e] = -__builtin_huge_valf();
         // Each team owns the tiles j of its parity and carries three list
         // entries in scalar registers: e_prev (tile j-2, whose PV runs in
         // phase j), e_cur (tile j: softmax and V fetch in phase j+1) and
@@ -910,59 +921,56 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
     if (g.n_hi > 0) section(std::integral_constant<int, kHi>{}, 0, g.n_hi);
     if (g.n_lo > 0) section(std::integral_constant<int, kLo>{}, g.n_hi, g.n_lo);
 
-    const int r = lane & 15, g4 = lane >> 4;
+    const int lq = lane & 31, lh = lane >> 5;
     // ---- merge the two teams: team 1 hands (m, l, acc) to team 0 through LDS ----
-    // 66 floats per lane (acc and l of both query tiles): 16896 B per wave,
-    // two waves per K slot
-    float* xch = reinterpret_cast<float*>(wq < 2 ? kslot0 : kslot1) + (size_t)(wq & 1) * (66 * 64);
+    // 65 floats per lane (acc and l): 16640 B per wave, two waves per K slot
+    float* xch = reinterpret_cast<float*>(wq < 2 ? kslot0 : kslot1) + (size_t)(wq & 1) * (65 * 64);
     if (team == 1) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) xch[((u * 8 + ct) * 4 + e) * 64 + lane] = st.acc[u][ct][e];
-            xch[(64 + u) * 64 + lane] = st.lsum[u][0];
-        }
+            for (int e = 0; e < 16; ++e) xch[(cb * 16 + e) * 64 + lane] = st.acc[cb][e];
+        xch[64 * 64 + lane] = st.lsum[0];
     }
-    float* xm = reinterpret_cast<float*>(vslot0) + wq * 128;     // m: 2 x 64 floats per wave
-    if (team == 1) {
-        xm[lane] = st.mref[0];
-        xm[64 + lane] = st.mref[1];
-    }
+    float* xm = reinterpret_cast<float*>(vslot0) + wq * 64;      // mref: 64 floats per wave
+    if (team == 1) xm[lane] = st.mref;
     __syncthreads();
     if (team == 1) return;
 
     const BlockPos qp = block_pos(g, qb);
     const int b = bh / g.heads;
     const int h = bh - b * g.heads;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const float m1 = xm[u * 64 + lane];
-        const float l1 = xch[(64 + u) * 64 + lane];
-        const float mm = fmaxf(st.mref[u], m1);
-        const float f0 = st.mref[u] > -__builtin_huge_valf() ? exp2f(st.mref[u] - mm) : 0.0f;
+    {
+        const float m1 = xm[lane];
+        const float l1 = xch[64 * 64 + lane];
+        const float mm = fmaxf(st.mref, m1);
+        const float f0 = st.mref > -__builtin_huge_valf() ? exp2f(st.mref - mm) : 0.0f;
         const float f1 = m1 > -__builtin_huge_valf() ? exp2f(m1 - mm) : 0.0f;
-        const float inv = 1.0f / (st.lsum[u][0] * f0 + l1 * f1);
-        const int qs = 32 * wq + 16 * u + r;
+        const float inv = 1.0f / (st.lsum[0] * f0 + l1 * f1);
+        const int qs = 32 * wq + lq;
         const int64_t n = slot_raster(g, qp, qs);
-        if (n < 0) continue;
-        const int64_t rowoff = (int64_t)b * g.stride_b + (int64_t)h * g.stride_h + n * g.stride_n;
+        if (n >= 0) {
+            const int64_t rowoff = (int64_t)b * g.stride_b + (int64_t)h * g.stride_h + n * g.stride_n;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            const int c = 16 * ct + 4 * g4;
-            if (c >= g.head_dim) continue;
-            float o[4];
+            for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                o[e] = (st.acc[u][ct][e] * f0 + xch[((u * 8 + ct) * 4 + e) * 64 + lane] * f1) * inv;
-            if (a.out_fp32) {
-                *reinterpret_cast<float4*>(static_cast<float*>(a.out) + rowoff + c) = make_float4(o[0], o[1], o[2], o[3]);
-            } else {
-                uint2 pk;
-                pk.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
-                pk.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + rowoff + c) = pk;
+                for (int jg = 0; jg < 4; ++jg) {
+                    const int c = 32 * cb + 8 * jg + 4 * lh;      // channels c .. c + 3
+                    if (c >= g.head_dim) continue;
+                    float o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o[e] = (st.acc[cb][4 * jg + e] * f0 + xch[(cb * 16 + 4 * jg + e) * 64 + lane] * f1) * inv;
+                    if (a.out_fp32) {
+                        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + rowoff + c) =
+                            make_float4(o[0], o[1], o[2], o[3]);
+                    } else {
+                        uint2 pk;
+                        pk.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
+                        pk.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + rowoff + c) = pk;
+                    }
+                }
             }
         }
     }
