@@ -9,63 +9,67 @@
 // Work decomposition (gfx950, wave64):
 //   one workgroup = one query block (128 slots) of one (batch, head), eight
 //   waves in two teams of four. Wave w%4 of either team owns query slots
-//   32(w%4) .. +32 as two 16-query tiles u. The query block's key tiles run
-//   as two sections, the hi list and then the lo list (each best-ranked
-//   first), so that every loop body has a single precision. Within a section
-//   the tiles alternate between the teams: team 0 takes tiles 0, 2, 4, ...,
-//   team 1 tiles 1, 3, 5, ...
+//   32(w%4) .. +32: lane l works for query l%32, the lanes l and l+32 (halves
+//   h = 0, 1) for the same query. The query block's key tiles run as two
+//   sections, the hi list and then the lo list (each best-ranked first), so
+//   that every loop body has a single precision. Within a section the tiles
+//   alternate between the teams: team 0 takes tiles 0, 2, 4, ..., team 1
+//   tiles 1, 3, 5, ...
 //   Time runs in phases separated by workgroup barriers. In phase p the team
 //   owning tile p runs its matrix work, PV of tile p-2 and QK^T of tile p,
 //   while the other team runs the softmax of tile p-1. The two waves sharing
-//   a SIMD are therefore always in opposite halves of their work: one keeps
-//   the MFMA pipe busy while the other exponentiates.
-//     S^T = K . Q^T        fp8 tiles: V_MFMA_F32_16X16X32_BF16 on the E4M3
+//   a SIMD are therefore always in opposite halves of their work: one feeds
+//   the matrix pipe while the other exponentiates.
+//     S^T = K . Q^T        fp8 tiles: V_MFMA_F32_32X32X16_BF16 on the E4M3
 //                          values widened to bf16 (exact): Q once by the
 //                          preparation kernel, K in registers from the E4M3
 //                          codes in LDS;
-//                          MXFP4 tiles: V_MFMA_SCALE_F32_16X16X128_F8F6F4
+//                          MXFP4 tiles: V_MFMA_SCALE_F32_32X32X64_F8F6F4
 //     softmax (base 2, integer running max per team, lane-local rescale)
-//     O^T += V^T . P^T     scaled f8f6f4 MFMAs (E4M3 or E2M1 operands), plus
-//                          one with an all-ones A that yields the row sum
-//                          l = sum P~ in the same lanes as O.
+//     O^T += V^T . P^T     scaled 32x32x64 f8f6f4 MFMAs (E4M3 or E2M1
+//                          operands), plus one with an all-ones A that yields
+//                          the row sum l = sum P~ in the same lanes as O.
+//   The 32x32 shapes issue half the MFMA instructions of the 16x16 ones for
+//   the same work, and on gfx950 an MFMA costs about the same issue time at
+//   either size: issue, not the matrix pipe, bounds this kernel.
 //   The query block's Q operands (bf16 and E2M1) sit in LDS for the whole
 //   kernel. K and V^T of a tile travel by direct global->LDS DMA into
-//   separate two-slot pools: K of tile p+1 and V^T of tile p-1 are issued at
-//   the start of phase p by the team running the softmax (a DMA instruction
-//   holds only the wave that issues it, so the matrix wave sharing its SIMD
-//   keeps issuing). The tile list entries each team needs travel in scalar
-//   registers, read from LDS one trip ahead. At the end the teams' (max, sum, accumulator) triples merge
-//   exactly: their maxima are integers, so the rescale factors are powers of
-//   two. Padded key slots are excluded by starting the QK^T accumulator at a
-//   per-slot bias (0 or -inf) that travels with K.
+//   separate two-slot pools: K of tile p+1 and V^T of tile p-1 are issued
+//   during phase p by the team running the softmax (a DMA instruction holds
+//   only the wave that issues it, so the matrix wave sharing its SIMD keeps
+//   issuing). The tile list entries each team needs travel in scalar
+//   registers, read from LDS one trip ahead. At the end the teams' (max, sum,
+//   accumulator) triples merge exactly: their maxima are integers, so the
+//   rescale factors are powers of two. Padded key slots are excluded by
+//   starting the QK^T accumulator at a per-slot bias (0 or -inf) that travels
+//   with K.
 //
-//   Computing S transposed makes each lane hold 32 keys of one query, which
-//   is exactly the B-operand layout of the PV product: P never leaves the
-//   lane, the MXFP4 group of P is the lane's own 32 values, and the max
-//   reduction needs two cross-lane steps (permlane swaps of 32 and 16 lanes).
+//   Computing S transposed makes each lane hold 64 keys of one query (the
+//   other 64 in its partner lane), which is exactly the B-operand layout of
+//   the PV product: P never leaves the lane, each MXFP4 group of P is 32 of
+//   the lane's own values, and the max reduction needs one cross-lane step.
 //
 //   Register budget: two waves per SIMD leave 256 registers per wave, of
 //   which the accumulator takes 64 and the scores another 64. The code is
 //   shaped so the allocator needs no copies or spills in the loops: static
-//   slot parity, no precision branches inside a loop body, values derived
-//   from the lane index recomputed where used, E2M1 operands kept as four
-//   dwords, and the rare rescale done in place.
+//   slot parity, no precision branches and no per-phase conditions inside a
+//   loop body, values derived from the lane index recomputed where used,
+//   E2M1 operands kept as four dwords, and the rare rescale done in place.
 //
-//   The fp8 tiles' QK^T runs on bf16 MFMAs because the f8f6f4 MFMA keeps only
-//   about 12 bits below its largest product when it sums fp8 products: with
-//   outlier channels the scores move by ~1e-2 (log2 units), enough to flip the
-//   rounding of many P codes. Their PV product stays fp8: nothing is decided
-//   from its rounding.
+//   The fp8 tiles' QK^T runs on bf16 MFMAs because the f8f6f4 MFMAs keep only
+//   about 12 bits below their largest product when they sum fp8 products:
+//   with outlier channels the scores move by ~1e-2 (log2 units), enough to
+//   flip the rounding of many P codes. Their PV product stays fp8: nothing is
+//   decided from its rounding.
 //
-// Operand layouts (measured on gfx950): a 16x16x128 fp8 operand lane l holds
-// row l%16 and bytes j -> k = 64*(j/16) + 16*(l/16) + j%16; an fp4 operand
-// lane l holds row l%16 and nibble j -> k = 32*(l/16) + j; the E8M0 scale of
-// lane l belongs to (row l%16, k-block l/16); D lane l element e is
-// D[4*(l/16) + e][l%16]. A 16x16x32 bf16 MFMA only needs A and B to share
-// their lane/k assignment. The key slot fed to A-row r of key sub-tile t is
-// chosen so that P's register order matches the PV k order:
-//   fp8:  slot = 64*(t/4) + 16*(r/4) + 4*(t%4) + r%4
-//   fp4:  slot = 32*(r/4) + 4*t + r%4          (k-block g = slots 32g..32g+31)
+// Operand layouts of the 32x32 MFMAs (gfx950): A lane l holds row l%32 and B
+// lane l column l%32, both for the same half h = l/32 of the k range (an E2M1
+// operand: nibble i -> k = 32 h + i, whose E8M0 scale lane l supplies); the
+// result D lane l element j is D[8*(j/4) + 4*h + j%4][l%32]. A and B only
+// need to agree on which k each lane byte carries. The key slot fed to A row
+// r of QK^T key block kb (sigma_fp8, sigma_fp4) is chosen so that the keys
+// whose P a lane holds for one PV MFMA are the slots that lane's V^T operand
+// reads in natural order.
 #include <type_traits>
 #include <utility>
 
