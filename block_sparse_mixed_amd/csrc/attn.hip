@@ -826,8 +826,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
         auto mma_phase = [&](auto par, int p, int32_t ev) __attribute__((always_inline)) {
             constexpr int PAR = decltype(par)::value;
             // In fp8 phases the matrix work is the longer: when both waves of
-            // a SIMD can issue, this one goes first (measured: 2 % faster;
-            // the same in MXFP4 phases, or for the softmax wave, is slower).
+            // a SIMD can issue, this one goes first (in MXFP4 phases the
+            // softmax wave does; either other choice measured slower).
             if constexpr (PH == kHi) __builtin_amdgcn_s_setprio(2);
             // the lane coordinates are recomputed here, not kept live
             const int ln = fresh_lane();
@@ -856,7 +856,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
                 constexpr int I = decltype(item)::value;
                 if constexpr (I < kFetchItems<PH>) fetch_item<PH, I>(tk, ks, tv, vs, wq, ln, o);
             };
+            // in MXFP4 phases the softmax is the longer work: it issues first
+            if constexpr (PH == kLo) __builtin_amdgcn_s_setprio(2);
             softmax<PH>(st, s, tile(p - 1, ek).e_k, pop, psc, hook);
+            if constexpr (PH == kLo) __builtin_amdgcn_s_setprio(0);
         };
         // a list entry read from LDS at the start of a phase becomes a scalar
         // at its end, after the phase's work has hidden the LDS latency
