@@ -35,9 +35,10 @@
 //   The query block's Q operands (bf16 and E2M1) sit in LDS for the whole
 //   kernel. K and V^T of a tile travel by direct global->LDS DMA into
 //   separate two-slot pools: K of tile p+1 and V^T of tile p-1 are issued
-//   during phase p by the team running the softmax (a DMA instruction holds
-//   only the wave that issues it, so the matrix wave sharing its SIMD keeps
-//   issuing). The tile list entries each team needs travel in scalar
+//   during phase p by the team running the softmax, between its maximum and
+//   its exponentials (a DMA instruction holds only the wave that issues it,
+//   so the matrix wave sharing its SIMD keeps issuing, and the
+//   exponentials hide the DMA latency). The tile list entries each team needs travel in scalar
 //   registers, read from LDS one trip ahead. At the end the teams' (max, sum,
 //   accumulator) triples merge exactly: their maxima are integers, so the
 //   rescale factors are powers of two. Padded key slots are excluded by
@@ -492,17 +493,22 @@ __device__ __forceinline__ float cross2max(float v) {
 // two, and mref moved to m.
 //   P operand of PV MFMA n (keys 64 n .. 64 n + 63 of the PV order): the
 // lane's scores of key blocks 2 n and 2 n + 1, in register order.
+//   fetch() issues the phase's DMA. In fp8 phases it is called after the
+// maximum, in MXFP4 phases after the P codes and scales; in both, the
+// compiler then places the exponentials (pure, and read only in the next
+// phase) after the DMA instructions, so that the exponentials hide the DMA
+// latency before the phase's closing barrier. Measured slower: the DMA
+// before the maximum, spread among the exponentials, or forced after them.
 constexpr float kMaxLead = 64.0f;
 
-template <int PH, class Hook>
+template <int PH, class Fetch>
 __device__ __forceinline__ void softmax(WaveState& st, const v16f (&s)[4], int e_k, v8i (&pop)[2], int (&psc)[2],
-                                        Hook&& hook) {
+                                        Fetch&& fetch) {
     const float cs = PH == kHi ? ldexpf(st.c_hi_q, e_k) : st.c_lo;
     float gmax[2];                                       // per PV MFMA n: the lane's 32 raw scores
 #pragma unroll
     for (int n = 0; n < 2; ++n) gmax[n] = max32(s[2 * n], s[2 * n + 1]);
     const float mnew = fmaxf(st.m, ceilf(cross2max(vmax(gmax[0], gmax[1])) * cs));
-    hook(std::integral_constant<int, 0>{});
     if (!(st.mref >= mnew - kMaxLead)) {
         const float f = exp2f(st.mref - mnew);           // 0 while mref = -inf
 #pragma unroll
@@ -510,6 +516,7 @@ __device__ __forceinline__ void softmax(WaveState& st, const v16f (&s)[4], int e
         scale_in_place(st.lsum, f);
         st.mref = mnew;
     }
+    if constexpr (PH == kHi) fetch();
     static_for<2>([&](auto nc) __attribute__((always_inline)) {
         constexpr int n = decltype(nc)::value;
         if constexpr (PH == kHi) {
@@ -524,10 +531,6 @@ __device__ __forceinline__ void softmax(WaveState& st, const v16f (&s)[4], int e
                                             __builtin_amdgcn_exp2f(__builtin_fmaf(x[j + 1], cs, off)),
                                             __builtin_amdgcn_exp2f(__builtin_fmaf(x[j + 2], cs, off)),
                                             __builtin_amdgcn_exp2f(__builtin_fmaf(x[j + 3], cs, off)));
-                if constexpr ((d & 1) == 1) {
-                    hook(std::integral_constant<int, 1 + 4 * n + (d >> 1)>{});
-                    fence();
-                }
             });
             // 127 .. 127 + kMaxLead (127 while no key has been seen: both -inf)
             psc[n] = 127 + (int)fmaxf(mnew - st.mref, 0.0f);
@@ -546,14 +549,13 @@ __device__ __forceinline__ void softmax(WaveState& st, const v16f (&s)[4], int e
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j + e], cs, off));
                 pop[n][d] = (int)pack_fp4x8(v);
-                hook(std::integral_constant<int, 1 + 4 * n + d>{});
-                fence();
             });
             const int sc = any ? (int)(F - st.mref) + 8 + 127 : 0;
             psc[n] = min(254, max(0, sc));
         }
     });
     st.m = mnew;
+    if constexpr (PH == kLo) fetch();
 }
 
 // ---- O^T += V^T . P^T and l += 1 . P^T ----
@@ -852,13 +854,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
             const Tile tv = tile(p - 1, fv);
             uint8_t* ks = PAR ? kslot0 : kslot1;
             uint8_t* vs = PAR ? vslot0 : vslot1;
-            auto hook = [&](auto item) __attribute__((always_inline)) {
-                constexpr int I = decltype(item)::value;
-                if constexpr (I < kFetchItems<PH>) fetch_item<PH, I>(tk, ks, tv, vs, wq, ln, o);
+            auto fetch = [&]() __attribute__((always_inline)) {
+                static_for<kFetchItems<PH>>([&](auto item) __attribute__((always_inline)) {
+                    fetch_item<PH, decltype(item)::value>(tk, ks, tv, vs, wq, ln, o);
+                    fence();
+                });
             };
             // in MXFP4 phases the softmax is the longer work: it issues first
             if constexpr (PH == kLo) __builtin_amdgcn_s_setprio(2);
-            softmax<PH>(st, s, tile(p - 1, ek).e_k, pop, psc, hook);
+            softmax<PH>(st, s, tile(p - 1, ek).e_k, pop, psc, fetch);
             if constexpr (PH == kLo) __builtin_amdgcn_s_setprio(0);
         };
         // a list entry read from LDS at the start of a phase becomes a scalar
