@@ -117,12 +117,14 @@ constexpr int kQb = 0, kQ4 = 32768, kQs = 40960, kQBytes = 41472;
 constexpr int kListBytes = 4 * DA2_MAX_BLOCKS;    // packed tile list
 static_assert(2 * 65 * 64 * 4 <= kKSlot, "team merge area: two waves per K slot");
 
-// LDS swizzles (16-byte chunk index XOR a row function) so that the eight
-// lanes served together by a 128-bit LDS read hit distinct banks.
-__device__ __forceinline__ int swz_k8f(int s) { return ((s >> 1) & 1) | (((s >> 4) & 1) << 1); }
-__device__ __forceinline__ int swz_v8(int c) { return c & 7; }
-__device__ __forceinline__ int swz_k4(int s) { return ((s >> 1) & 1) | ((s >> 4) & 2); }
-__device__ __forceinline__ int swz_v4(int c) { return (c >> 1) & 3; }
+// LDS swizzles (16-byte chunk index XOR a row function) so that the sixteen
+// lanes served together by a 128-bit LDS read (64 banks of 4 bytes) hit
+// sixteen distinct 16-byte bank groups; each depends only on the lane's
+// query or channel index, not on the step.
+__device__ __forceinline__ int swz_k8f(int s) { return ((s >> 1) & 1) | (((s >> 4) & 1) << 1) | (((s >> 2) & 1) << 2); }
+__device__ __forceinline__ int swz_v8(int c) { return (c >> 1) & 7; }
+__device__ __forceinline__ int swz_k4(int s) { return ((s >> 2) & 1) | ((s >> 4) & 2); }
+__device__ __forceinline__ int swz_v4(int c) { return (c >> 2) & 3; }
 
 // The key slot fed to A row r (0 .. 31) of QK^T key block kb (0 .. 3). A
 // 32x32 MFMA result row r sits in lane half (r / 4) % 2 at register
@@ -178,12 +180,16 @@ struct DmaOffsets {
 
 __device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
     DmaOffsets o;
-    o.v8 = ((lane >> 3) << 7) + (((lane & 7) ^ (lane >> 3)) << 4);
-    o.k4 = ((lane >> 2) << 6) + (((lane & 3) ^ ((lane >> 3) & 1)) << 4);
-    o.v4 = ((lane >> 2) << 6) + (((lane & 3) ^ ((lane >> 3) & 3)) << 4);
+    // E4M3 V^T rows (128 B): a DMA of channels 8i .. 8i+7 gathers with this
+    // offset XOR ((i & 1) << 6)
+    o.v8 = ((lane >> 3) << 7) + (((lane & 7) ^ ((lane >> 4) & 3)) << 4);
+    // E2M1 K rows (64 B): a DMA of slots 16i .. 16i+15 gathers with this
+    // offset XOR ((i & 2) << 4)
+    o.k4 = ((lane >> 2) << 6) + (((lane & 3) ^ ((lane >> 4) & 1)) << 4);
+    o.v4 = ((lane >> 2) << 6) + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
     // E4M3 K rows (128 B): chunk c of row s sits at c ^ swz_k8f(s); a DMA of
     // rows 8i .. 8i+7 gathers with this offset XOR (((i >> 1) & 1) << 5)
-    o.k8f = ((lane >> 3) << 7) + (((lane & 7) ^ ((lane >> 4) & 1)) << 4);
+    o.k8f = ((lane >> 3) << 7) + (((lane & 7) ^ ((lane >> 4) & 1) ^ (((lane >> 5) & 1) << 2)) << 4);
     return o;
 }
 
@@ -246,7 +252,7 @@ __device__ __forceinline__ void k_row(const Tile& t, uint8_t* slot, int wr, cons
 template <int PH>
 __device__ __forceinline__ void v_row(const Tile& t, uint8_t* slot, int wr, const DmaOffsets& o) {
     if constexpr (PH == kHi)   // 16 KiB of E4M3 V^T
-        dma16(t.v + wr * 1024 + o.v8, slot + wr * 1024);
+        dma16(t.v + wr * 1024 + (o.v8 ^ ((wr & 1) << 6)), slot + wr * 1024);
     else                       // 8 KiB of E2M1 V^T
         dma16(t.v + wr * 1024 + o.v4, slot + wr * 1024);
 }
@@ -305,8 +311,8 @@ __device__ __forceinline__ v8i fp4_operand(v4i x) {
 __device__ __forceinline__ v4i as_v4i(const uint4& x) { return (v4i){(int)x.x, (int)x.y, (int)x.z, (int)x.w}; }
 
 // ---- Q operands of the wave's 32 queries, read from LDS ----
-// Q rows in LDS are swizzled like the K rows: bf16 16-byte chunk c of query
-// slot q sits at chunk c ^ (q & 7); E2M1 chunk c at c ^ ((q >> 1) & 3).
+// Q rows in LDS are swizzled: bf16 16-byte chunk c of query slot q sits at
+// chunk c ^ (q & 15); E2M1 chunk c at c ^ ((q >> 2) & 3).
 // Lane (query q, half h) feeds the bf16 MFMAs channels 32 i + 16 h .. + 15
 // (two MFMAs of 8 channels per i) and the E2M1 MFMAs channels 64 c + 32 h ..
 // + 31; K uses the same assignment.
@@ -318,19 +324,19 @@ struct QOps {
 
 template <int PH>
 __device__ __forceinline__ void load_q(const WaveState& st, QOps& qo, int q, int h) {
-    const int qs = st.qs0 + q;                 // qs & 7 == q & 7: qs0 is a multiple of 32
+    const int qs = st.qs0 + q;                 // qs & 31 == q: qs0 is a multiple of 32
     if constexpr (PH == kHi) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int e = 0; e < 2; ++e)
                 qo.qb[i][e] = __builtin_bit_cast(
-                    v8bf, *reinterpret_cast<const uint4*>(st.q + kQb + qs * 256 + (((4 * i + 2 * h + e) ^ (q & 7)) << 4)));
+                    v8bf, *reinterpret_cast<const uint4*>(st.q + kQb + qs * 256 + (((4 * i + 2 * h + e) ^ (q & 15)) << 4)));
     } else {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int chunk = 2 * c + h;
-            qo.q4[c] = as_v4i(*reinterpret_cast<const uint4*>(st.q + kQ4 + qs * 64 + ((chunk ^ ((q >> 1) & 3)) << 4)));
+            qo.q4[c] = as_v4i(*reinterpret_cast<const uint4*>(st.q + kQ4 + qs * 64 + ((chunk ^ ((q >> 2) & 3)) << 4)));
             qo.q4s[c] = st.q[kQs + qs * 4 + chunk];
         }
     }
@@ -699,7 +705,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
             const int wr = w + kWaves * n;
             const int p = wr * 64 + lane;
             const int q = p >> 4, pc = p & 15;
-            dma16(qb_src + (q * 16 + (pc ^ (q & 7))) * 16, qlds + kQb + wr * 1024);
+            dma16(qb_src + (q * 16 + (pc ^ (q & 15))) * 16, qlds + kQb + wr * 1024);
         }
         const uint8_t* q4_src = ws + a.L.q4 + qtile * (DA2_TILE * DA2_DPAD / 2);
 #pragma unroll
@@ -707,7 +713,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
             const int wr = w + kWaves * n;
             const int p = wr * 64 + lane;
             const int q = p >> 2, pc = p & 3;
-            dma16(q4_src + (q * 4 + (pc ^ ((q >> 1) & 3))) * 16, qlds + kQ4 + wr * 1024);
+            dma16(q4_src + (q * 4 + (pc ^ ((q >> 2) & 3))) * 16, qlds + kQ4 + wr * 1024);
         }
         if (w == 2 && lane < 32)
             dma16(ws + a.L.sq4 + qtile * (DA2_TILE * DA2_DPAD / 32) + lane * 16, qlds + kQs);
