@@ -368,35 +368,42 @@ __device__ __forceinline__ void qk(const uint8_t* ks, QOps& qo, v16f (&s)[4], in
 #pragma unroll
         for (int i = 0; i < 4; ++i) kp[i] = ks + rho * 128 + (((2 * i + h) ^ sw) << 4);
         const uint8_t* bp = ks + kKBias + 64 * h;
-        // one step = (kb, i): 16 E4M3 codes, widened, feed two MFMAs; the
-        // codes of the next step are read first
-        uint4 code[2];
-        code[0] = *reinterpret_cast<const uint4*>(kp[0]);
+        // the accumulators start at the bias, all read up front
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            v16f d;
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) {
                 const v4f b4 = *reinterpret_cast<const v4f*>(bp + 128 * kb + 16 * e4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) d[4 * e4 + e] = b4[e];
+                for (int e = 0; e < 4; ++e) s[kb][4 * e4 + e] = b4[e];
             }
+        // one step = (kb, i): 16 E4M3 codes, widened, feed two MFMAs; the
+        // codes are read 2 - 1 steps ahead (the fence after each read keeps
+        // the scheduler from sinking it towards its use)
+        constexpr int R = 2;
+        uint4 code[R];
+#pragma unroll
+        for (int t = 0; t + 1 < R; ++t) code[t] = *reinterpret_cast<const uint4*>(kp[t & 3] + 4096 * (t >> 2));
+        fence();
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int step = 4 * kb + i;
-                if (step + 1 < 16)
-                    code[(step + 1) & 1] =
-                        *reinterpret_cast<const uint4*>(kp[(step + 1) & 3] + 4096 * ((step + 1) >> 2));
-                const uint4& x = code[step & 1];
+                if (step + R - 1 < 16) {
+                    code[(step + R - 1) % R] =
+                        *reinterpret_cast<const uint4*>(kp[(step + R - 1) & 3] + 4096 * ((step + R - 1) >> 2));
+                    fence();
+                }
+                const uint4& x = code[step % R];
                 v8bf kb0 = widen_e4m3(x.x, x.y);
                 v8bf kb1 = widen_e4m3(x.z, x.w);
-                d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb0, qo.qb[i][0], d, 0, 0, 0);
-                d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb1, qo.qb[i][1], d, 0, 0, 0);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb0, qo.qb[i][0], s[kb], 0, 0, 0);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb1, qo.qb[i][1], s[kb], 0, 0, 0);
                 keep(kb0);
                 keep(kb1);
                 fence();
             }
-            s[kb] = d;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -458,25 +465,29 @@ __device__ __forceinline__ void scale_in_place(v16f& x, float f) {
     }
 }
 
-// Plain V_MAX3_F32 / V_MAX_F32: the scores are never NaN, so the NaN-quieting
-// moves that fmaxf adds in front of a maximum of MFMA results are not needed.
-__device__ __forceinline__ float vmax3(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-__device__ __forceinline__ float vmax(float a, float b) {
-    float r;
-    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
-}
+// IEEE maximum (V_MAXIMUM3_F32 on gfx950). The scores are never NaN, so it
+// equals the usual max here; unlike fmaxf it needs no NaN-quieting move in
+// front of an MFMA result, and unlike a hand-written V_MAX3_F32 the compiler
+// knows it is a plain ALU op and adds no wait states after it.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 
-// The maximum of 32 scores (two key blocks): one chain of three-input maxima.
-__device__ __forceinline__ float max32(const v16f& x, const v16f& y) {
-    float a = vmax3(x[0], x[1], x[2]);
+// The lane's maximum over each pair of key blocks (2n, 2n+1): four chains of
+// three-input maxima, one per key block, advanced in lockstep so that no
+// step waits on the step before it (one dependent chain needs a wait state
+// between its steps).
+__device__ __forceinline__ void block_max(const v16f (&s)[4], float (&gmax)[2]) {
+    float a[4];
 #pragma unroll
-    for (int i = 3; i + 1 < 32; i += 2) a = vmax3(a, i < 16 ? x[i] : y[i - 16], i + 1 < 16 ? x[i + 1] : y[i - 15]);
-    return vmax(a, y[15]);
+    for (int k = 0; k < 4; ++k) a[k] = vmax3(s[k][0], s[k][1], s[k][2]);
+#pragma unroll
+    for (int i = 3; i + 1 < 16; i += 2)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a[k] = vmax3(a[k], s[k][i], s[k][i + 1]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = vmax(a[k], s[k][15]);
+    gmax[0] = vmax(a[0], a[1]);
+    gmax[1] = vmax(a[2], a[3]);
 }
 
 // Max over the two lanes l and l ^ 32 (the query's two halves of keys): the
@@ -512,8 +523,7 @@ __device__ __forceinline__ void softmax(WaveState& st, const v16f (&s)[4], int e
                                         Fetch&& fetch) {
     const float cs = PH == kHi ? ldexpf(st.c_hi_q, e_k) : st.c_lo;
     float gmax[2];                                       // per PV MFMA n: the lane's 32 raw scores
-#pragma unroll
-    for (int n = 0; n < 2; ++n) gmax[n] = max32(s[2 * n], s[2 * n + 1]);
+    block_max(s, gmax);
     const float mnew = fmaxf(st.m, ceilf(cross2max(vmax(gmax[0], gmax[1])) * cs));
     if (!(st.mref >= mnew - kMaxLead)) {
         const float f = exp2f(st.mref - mnew);           // 0 while mref = -inf
