@@ -78,22 +78,39 @@ __global__ __launch_bounds__(256) void draft_logits_kernel(Geo g, const double* 
         }
 }
 
-__device__ __forceinline__ double block_reduce_max(double v, double* red) {
-    for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+// Workgroup (four waves) maximum and sum of two values at once; each value
+// is reduced exactly as a reduction of its own would (butterfly within the
+// wave, then the four wave results in a fixed order).
+__device__ __forceinline__ void block_reduce_max2(double& a, double& b, double* red) {
+    for (int off = 32; off > 0; off >>= 1) {
+        a = fmax(a, __shfl_xor(a, off));
+        b = fmax(b, __shfl_xor(b, off));
+    }
     const int w = threadIdx.x >> 6;
     __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[w] = v;
+    if ((threadIdx.x & 63) == 0) {
+        red[w] = a;
+        red[4 + w] = b;
+    }
     __syncthreads();
-    return fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+    a = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+    b = fmax(fmax(red[4], red[5]), fmax(red[6], red[7]));
 }
 
-__device__ __forceinline__ double block_reduce_sum(double v, double* red) {
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+__device__ __forceinline__ void block_reduce_sum2(double& a, double& b, double* red) {
+    for (int off = 32; off > 0; off >>= 1) {
+        a += __shfl_xor(a, off);
+        b += __shfl_xor(b, off);
+    }
     const int w = threadIdx.x >> 6;
     __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[w] = v;
+    if ((threadIdx.x & 63) == 0) {
+        red[w] = a;
+        red[4 + w] = b;
+    }
     __syncthreads();
-    return (red[0] + red[1]) + (red[2] + red[3]);
+    a = (red[0] + red[1]) + (red[2] + red[3]);
+    b = (red[4] + red[5]) + (red[6] + red[7]);
 }
 
 // Write the ascending lists of blocks labelled want (at most cap entries);
@@ -112,44 +129,163 @@ __device__ __forceinline__ int compact_list(const int8_t* lab, int nb, int8_t wa
     return count;
 }
 
+// "a before b" in rank order: larger C first, then the lower block index.
+__device__ __forceinline__ bool before(double va, int ia, double vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
+// Bitonic sort of np = 256 R (value, index) pairs held in registers: lane l
+// of wave w holds elements 64 R w + R l .. + R - 1. A compare-exchange step
+// of partner distance jj runs inside the lane (jj < R), across lanes of the
+// wave by shuffles (jj < 64 R), or across waves through LDS (the only steps
+// with workgroup barriers). The pairs start in and return to val/idx.
+template <int R>
+struct SortState {
+    double v[R];
+    int ix[R];
+};
+
+// One compare-exchange step of stage k, partner distance jj: element e ends
+// up holding the first of the pair (e, e ^ jj) when it is the lower element
+// of an ascending pair or the upper element of a descending one.
+template <int R>
+__device__ __forceinline__ void bitonic_step(SortState<R>& st, double* val, int32_t* idx, int base, int k, int jj) {
+    if (jj < R) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (r & jj) continue;
+            const int r2 = r | jj;
+            const bool fwd = ((base + r) & k) == 0;
+            const bool swap = fwd != before(st.v[r], st.ix[r], st.v[r2], st.ix[r2]);
+            const double a = st.v[r], b = st.v[r2];
+            const int ia = st.ix[r], ib = st.ix[r2];
+            st.v[r] = swap ? b : a;
+            st.v[r2] = swap ? a : b;
+            st.ix[r] = swap ? ib : ia;
+            st.ix[r2] = swap ? ia : ib;
+        }
+        return;
+    }
+    double pv[R];
+    int pi[R];
+    if (jj < 64 * R) {
+        const int d = jj / R;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            pv[r] = __shfl_xor(st.v[r], d);
+            pi[r] = __shfl_xor(st.ix[r], d);
+        }
+    } else {
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            val[base + r] = st.v[r];
+            idx[base + r] = st.ix[r];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            pv[r] = val[(base + r) ^ jj];
+            pi[r] = idx[(base + r) ^ jj];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int e = base + r;
+        const bool want_first = ((e & jj) == 0) == ((e & k) == 0);
+        const bool take = before(st.v[r], st.ix[r], pv[r], pi[r]) != want_first;
+        st.v[r] = take ? pv[r] : st.v[r];
+        st.ix[r] = take ? pi[r] : st.ix[r];
+    }
+}
+
+// compile-time stages for the small sizes (every condition of a step folds
+// away); a plain loop for the large ones, whose full unrolling is too big
+template <int R, int K, int JJ>
+__device__ __forceinline__ void bitonic_stages(SortState<R>& st, double* val, int32_t* idx, int base) {
+    if constexpr (K <= 256 * R) {
+        bitonic_step<R>(st, val, idx, base, K, JJ);
+        if constexpr (JJ > 1)
+            bitonic_stages<R, K, JJ / 2>(st, val, idx, base);
+        else
+            bitonic_stages<R, 2 * K, K>(st, val, idx, base);
+    }
+}
+
+// Bitonic sort of np = 256 R (value, index) pairs held in registers: lane l
+// of wave w holds elements 64 R w + R l .. + R - 1. A compare-exchange step
+// of partner distance jj runs inside the lane (jj < R), across lanes of the
+// wave by shuffles (jj < 64 R), or across waves through LDS (the only steps
+// with workgroup barriers). The pairs start in and return to val/idx.
+template <int R>
+__device__ __forceinline__ void bitonic_sort(double* val, int32_t* idx) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int base = 64 * R * w + R * lane;
+    SortState<R> st;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        st.v[r] = val[base + r];
+        st.ix[r] = idx[base + r];
+    }
+    if constexpr (R <= 2) {
+        bitonic_stages<R, 2, 1>(st, val, idx, base);
+    } else {
+        for (int k = 2; k <= 256 * R; k <<= 1)
+            for (int jj = k >> 1; jj > 0; jj >>= 1) bitonic_step<R>(st, val, idx, base, k, jj);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        val[base + r] = st.v[r];
+        idx[base + r] = st.ix[r];
+    }
+    __syncthreads();
+}
+
+// R = np / 256 pairs per thread in the sort (a template parameter, so that
+// each size gets its own register allocation)
+template <int R>
 __global__ __launch_bounds__(256) void rank_kernel(Geo g, double* __restrict__ scores, int8_t* __restrict__ labels,
                                                    int32_t* __restrict__ hi_list, int32_t* __restrict__ lo_list) {
     const int i = blockIdx.x;
     const int bh = blockIdx.y;
     const int nb = g.n_blocks;
     const int tid = threadIdx.x;
-    int np = 1;
-    while (np < nb) np <<= 1;
+    const int np = 256 * R;         // a power of two, at least nb and one pair per thread
 
     extern __shared__ __align__(16) unsigned char smem[];
     double* val = reinterpret_cast<double*>(smem);              // [np]
-    int32_t* idx = reinterpret_cast<int32_t*>(val + np);        // [np]
+    double* val2 = val + np;                                    // [np]
+    int32_t* idx = reinterpret_cast<int32_t*>(val2 + np);       // [np]
     int8_t* lab = reinterpret_cast<int8_t*>(idx + np);          // [np]
-    __shared__ double red[4];
+    __shared__ double red[8];
 
     double* row_avg = scores + ((uint64_t)bh * nb + i) * nb;
     double* row_max = scores + (uint64_t)g.bh * nb * nb + ((uint64_t)bh * nb + i) * nb;
 
-    // combined score C = (softmax(avg row) + softmax(max row)) / 2
-    double mx = -__builtin_huge_val();
-    for (int j = tid; j < nb; j += 256) mx = fmax(mx, row_avg[j]);
-    mx = block_reduce_max(mx, red);
-    double sm = 0.0;
+    // combined score C = (softmax(avg row) + softmax(max row)) / 2; both rows
+    // are read from global memory once, into LDS
+    double mx = -__builtin_huge_val(), mx2 = -__builtin_huge_val();
     for (int j = tid; j < nb; j += 256) {
-        const double e = exp(row_avg[j] - mx);
-        val[j] = e;
-        sm += e;
+        const double va = row_avg[j], vm = row_max[j];
+        val[j] = va;
+        val2[j] = vm;
+        mx = fmax(mx, va);
+        mx2 = fmax(mx2, vm);
     }
-    sm = block_reduce_sum(sm, red);
-    double mx2 = -__builtin_huge_val();
-    for (int j = tid; j < nb; j += 256) mx2 = fmax(mx2, row_max[j]);
-    mx2 = block_reduce_max(mx2, red);
-    double sm2 = 0.0;
-    for (int j = tid; j < nb; j += 256) sm2 += exp(row_max[j] - mx2);
-    sm2 = block_reduce_sum(sm2, red);
+    block_reduce_max2(mx, mx2, red);
+    double sm = 0.0, sm2 = 0.0;
+    for (int j = tid; j < nb; j += 256) {
+        const double e = exp(val[j] - mx), e2 = exp(val2[j] - mx2);
+        val[j] = e;
+        val2[j] = e2;
+        sm += e;
+        sm2 += e2;
+    }
+    block_reduce_sum2(sm, sm2, red);
     for (int j = tid; j < np; j += 256) {
         if (j < nb) {
-            const double c = 0.5 * (val[j] / sm + exp(row_max[j] - mx2) / sm2);
+            const double c = 0.5 * (val[j] / sm + val2[j] / sm2);
             val[j] = c;
             idx[j] = j;
             row_avg[j] = c;     // section 0 of the scores now holds C for this row
@@ -160,41 +296,8 @@ __global__ __launch_bounds__(256) void rank_kernel(Geo g, double* __restrict__ s
     }
     __syncthreads();
 
-    // bitonic sort, "a before b" iff C_a > C_b or (C_a == C_b and index_a < index_b).
-    // Thread tid owns the compare pairs p = tid, tid + 256, ...; for a partner
-    // distance jj <= 64 the pairs of wave w touch only elements 128 w ..
-    // 128 w + 127 (and the same plus multiples of 512), so consecutive such
-    // steps need no workgroup barrier (a wave's LDS accesses complete in order).
-    for (int k = 2; k <= np; k <<= 1) {
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-            const int lg = __builtin_ctz(jj);
-            for (int p = tid; p < (np >> 1); p += 256) {
-                const int lo = ((p >> lg) << (lg + 1)) + (p & (jj - 1));
-                const int hi = lo + jj;
-                const double va = val[lo], vb = val[hi];
-                const int ia = idx[lo], ib = idx[hi];
-                const bool b_first = (vb > va) || (vb == va && ib < ia);
-                const bool a_first = (va > vb) || (va == vb && ia < ib);
-                const bool forward = (lo & k) == 0;
-                if (forward ? b_first : a_first) {
-                    val[lo] = vb;
-                    val[hi] = va;
-                    idx[lo] = ib;
-                    idx[hi] = ia;
-                }
-            }
-            // A workgroup barrier is needed when this step or the next one
-            // crosses waves (distance above 64); the next step's distance is
-            // jj / 2, or k when this stage ends. (With np > 512 a thread's
-            // second pair p + 256 lies 512 elements further, in the same
-            // wave's other chunk, which keeps small distances wave-local.)
-            if (jj > 64 || (jj == 1 && k > 64))
-                __syncthreads();
-            else
-                __builtin_amdgcn_wave_barrier();
-        }
-    }
-    __syncthreads();
+    // bitonic sort, "a before b" iff C_a > C_b or (C_a == C_b and index_a < index_b)
+    bitonic_sort<R>(val, idx);
     const int n_ret = g.n_hi + g.n_lo;
     for (int r = tid; r < nb; r += 256) lab[idx[r]] = (int8_t)(r < g.n_hi ? DA2_HI : (r < n_ret ? DA2_LO : DA2_SKIP));
     __syncthreads();
@@ -240,12 +343,21 @@ hipError_t launch_draft(const Geo& g, const Layout& L, void* ws, hipStream_t str
     const int t = (g.n_blocks + kTile - 1) / kTile;
     hipError_t e = launch_kernel(draft_logits_kernel, dim3(t, t, 2 * g.bh), dim3(256), 0, stream, g, pool, scores);
     if (e != hipSuccess) return e;
-    int np = 1;
+    int np = 256;
     while (np < g.n_blocks) np <<= 1;
-    const size_t shmem = (size_t)np * (8 + 4 + 1);
-    return launch_kernel(rank_kernel, dim3(g.n_blocks, g.bh), dim3(256), shmem, stream, g, scores,
-                       reinterpret_cast<int8_t*>(base + L.labels), reinterpret_cast<int32_t*>(base + L.hi),
-                       reinterpret_cast<int32_t*>(base + L.lo));
+    const size_t shmem = (size_t)np * (8 + 8 + 4 + 1);
+    auto run = [&](auto kernel) {
+        return launch_kernel(kernel, dim3(g.n_blocks, g.bh), dim3(256), shmem, stream, g, scores,
+                             reinterpret_cast<int8_t*>(base + L.labels), reinterpret_cast<int32_t*>(base + L.hi),
+                             reinterpret_cast<int32_t*>(base + L.lo));
+    };
+    switch (np >> 8) {
+        case 1: return run(rank_kernel<1>);
+        case 2: return run(rank_kernel<2>);
+        case 4: return run(rank_kernel<4>);
+        case 8: return run(rank_kernel<8>);
+        default: return run(rank_kernel<16>);      // np <= DA2_MAX_BLOCKS = 4096
+    }
 }
 
 hipError_t launch_set_labels(const Geo& g, const Layout& L, void* ws, const int8_t* labels, hipStream_t stream) {

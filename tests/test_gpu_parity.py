@@ -123,3 +123,15 @@ def test_edge_shapes(da2):
     ]
     for w in cases:
         _full_parity(da2, w)
+
+
+@pytest.mark.parametrize("grid", [66, 94])
+def test_prepare_large_block_counts(da2, grid):
+    # 2x2-token windows give 1089 and 2209 blocks: the ranking sorts 2048 and
+    # 4096 (score, index) pairs per row (eight and sixteen per thread), past
+    # the sizes the video workloads reach
+    w = dataclasses.replace(S.TINY, name=f"blocks{grid}", frames=1, grid_h=grid, grid_w=grid, win_h=2, win_w=2,
+                            head_dim=64, budget_hi=0.1, budget_lo=0.2)
+    run = GpuRun(da2, w)
+    say(f"check prepare {w.name} nb={run.nb}")
+    check_prepare(run, 0, run.oracle_head(0))
