@@ -761,19 +761,21 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
         }
     }
     __syncthreads();
-    // The key and value slots start zeroed, so that every byte in them is a
-    // finite code or scale: the empty tile's PV reads value slots that no
-    // fetch has written yet (with P = 0).
+    // The first fp8 section's first K tile is fetched now, under the rest of
+    // the prologue (team 1 fetches in the even phases).
+    if (g.n_hi > 0 && team == 1) {
+        const int ln = fresh_lane();
+        dma_k<kHi>(tile_from<kHi>(a, ws, bh, tl[0]), kslot0, wq, ln, dma_offsets(ln));
+    }
+    // Value slot 0 starts zeroed, so that every byte in it is a finite code
+    // or scale: the first phase's PV of a section (the empty tile, P = 0)
+    // reads it before any fetch has written it. Every other slot is written
+    // by a fetch before it is read; in an MXFP4 section slot 0 holds fp8
+    // codes (finite in either format) and, in its scale area, which fp8
+    // tiles leave untouched, these zeros.
     {
         const uint4 z = {0u, 0u, 0u, 0u};
-        for (int i = tid; i < kKSlot / 16; i += kThreads) {
-            reinterpret_cast<uint4*>(kslot0)[i] = z;
-            reinterpret_cast<uint4*>(kslot1)[i] = z;
-        }
-        for (int i = tid; i < kVSlot / 16; i += kThreads) {
-            reinterpret_cast<uint4*>(vslot0)[i] = z;
-            reinterpret_cast<uint4*>(vslot1)[i] = z;
-        }
+        for (int i = tid; i < kVSlot / 16; i += kThreads) reinterpret_cast<uint4*>(vslot0)[i] = z;
     }
 
     WaveState st;
@@ -889,8 +891,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
         };
         using Even = std::integral_constant<int, 0>;
         using Odd = std::integral_constant<int, 1>;
-        // the section's first K tile (team 1, which fetches in the even phases)
-        if (team == 1) {
+        // the section's first K tile (team 1, which fetches in the even
+        // phases; the fp8 section's was issued in the prologue)
+        if (PH == kLo && team == 1) {
             const int ln = fresh_lane();
             dma_k<PH>(tile(0, e_first), kslot0, wq, ln, dma_offsets(ln));
         }
