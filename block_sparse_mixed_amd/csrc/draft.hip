@@ -43,24 +43,26 @@ __global__ __launch_bounds__(256) void draft_logits_kernel(Geo g, const double* 
     const double* qp = pool + (uint64_t)(m) * plane + (uint64_t)bh * nb * DA2_DPAD;       // q avg / q max
     const double* kp = pool + (uint64_t)(2 + m) * plane + (uint64_t)bh * nb * DA2_DPAD;   // k avg / k max
 
-    __shared__ double qs[kTile][kKc + 1];
-    __shared__ double ks[kTile][kKc + 1];
+    // channel-major staging: thread (tx, ty) reads rows 4 ty .. 4 ty + 3 of
+    // Q and 4 tx .. 4 tx + 3 of K as two 16-byte reads each
+    __shared__ __align__(16) double qs[kKc][kTile + 2];
+    __shared__ __align__(16) double ks[kKc][kTile + 2];
     double acc[4][4] = {};
     for (int c0 = 0; c0 < g.head_dim; c0 += kKc) {
         for (int e = tid; e < kTile * kKc; e += 256) {
             const int r = e / kKc, cc = e % kKc;
-            qs[r][cc] = (i0 + r < nb) ? qp[(uint64_t)(i0 + r) * DA2_DPAD + c0 + cc] : 0.0;
-            ks[r][cc] = (j0 + r < nb) ? kp[(uint64_t)(j0 + r) * DA2_DPAD + c0 + cc] : 0.0;
+            qs[cc][r] = (i0 + r < nb) ? qp[(uint64_t)(i0 + r) * DA2_DPAD + c0 + cc] : 0.0;
+            ks[cc][r] = (j0 + r < nb) ? kp[(uint64_t)(j0 + r) * DA2_DPAD + c0 + cc] : 0.0;
         }
         __syncthreads();
 #pragma unroll 4
         for (int cc = 0; cc < kKc; ++cc) {
-            double qa[4], kb[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                qa[u] = qs[ty + 16 * u][cc];
-                kb[u] = ks[tx + 16 * u][cc];
-            }
+            const double2 q01 = *reinterpret_cast<const double2*>(&qs[cc][4 * ty]);
+            const double2 q23 = *reinterpret_cast<const double2*>(&qs[cc][4 * ty + 2]);
+            const double2 k01 = *reinterpret_cast<const double2*>(&ks[cc][4 * tx]);
+            const double2 k23 = *reinterpret_cast<const double2*>(&ks[cc][4 * tx + 2]);
+            const double qa[4] = {q01.x, q01.y, q23.x, q23.y};
+            const double kb[4] = {k01.x, k01.y, k23.x, k23.y};
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(256) void draft_logits_kernel(Geo g, const double* 
     for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const int i = i0 + ty + 16 * u, j = j0 + tx + 16 * w;
+            const int i = i0 + 4 * ty + u, j = j0 + 4 * tx + w;
             if (i < nb && j < nb) out[(uint64_t)i * nb + j] = g.tau * acc[u][w];
         }
 }
