@@ -52,7 +52,7 @@ class PlanInfo(ctypes.Structure):
         ("tokens", ctypes.c_int64), ("slots", ctypes.c_int64), ("tau", ctypes.c_double),
         ("workspace_bytes", ctypes.c_uint64),
     ] + [(n, ctypes.c_uint64) for n in (
-        "off_pool", "off_q8", "off_k8", "off_v8t", "off_e8", "off_q4", "off_k4", "off_v4t",
+        "off_pool", "off_k8", "off_v8t", "off_e8", "off_q4", "off_k4", "off_v4t",
         "off_sq4", "off_sk4", "off_sv4t", "off_scores", "off_labels", "off_hi", "off_lo", "off_status",
         "off_qb", "off_bias")]
 

@@ -18,7 +18,7 @@ struct Geo {
 };
 
 struct Layout {
-    uint64_t pool, q8, k8, qb, v8t, e8, q4, k4, v4t, sq4, sk4, sv4t, scores, labels, hi, lo, status, bias;
+    uint64_t pool, k8, qb, v8t, e8, q4, k4, v4t, sq4, sk4, sv4t, scores, labels, hi, lo, status, bias;
     uint64_t total;
 };
 

@@ -84,7 +84,6 @@ extern "C" da2_status da2_plan(const da2_config* cfg, da2_plan_t** out) {
     uint64_t off = 0;
     auto take = [&](uint64_t bytes) { uint64_t o = off; off = align256(off + bytes); return o; };
     L.pool = take(4 * B * N * P * 8);
-    L.q8 = take(B * N * T * P);
     L.k8 = take(B * N * T * P);
     L.qb = take(B * N * T * P * 2);
     L.v8t = take(B * N * P * T);
@@ -130,7 +129,6 @@ extern "C" da2_status da2_plan_info(const da2_plan_t* plan, da2_plan_info_t* out
     i.tau = g.tau;
     i.workspace_bytes = L.total;
     i.off_pool = L.pool;
-    i.off_q8 = L.q8;
     i.off_k8 = L.k8;
     i.off_v8t = L.v8t;
     i.off_e8 = L.e8;

@@ -94,7 +94,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
 
     if (tz < 2) {
         // ---- row pass (Q, K): E4M3 slot-major and MXFP4 along channels ----
-        uint8_t* c8 = a.ws + (tz == 0 ? a.L.q8 : a.L.k8) + tileid * (DA2_TILE * DA2_DPAD);
+        // (the Q codes are stored as their exact bf16 decode only)
+        uint8_t* c8 = a.ws + a.L.k8 + tileid * (DA2_TILE * DA2_DPAD);
         uint16_t* cb = reinterpret_cast<uint16_t*>(a.ws + a.L.qb) + tileid * (DA2_TILE * DA2_DPAD);
         uint8_t* c4 = a.ws + (tz == 0 ? a.L.q4 : a.L.k4) + tileid * (DA2_TILE * DA2_DPAD / 2);
         uint8_t* s4 = a.ws + (tz == 0 ? a.L.sq4 : a.L.sk4) + tileid * (DA2_TILE * DA2_DPAD / 32);
@@ -115,8 +116,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
             uint2 o8;
             o8.x = pack_fp8x4(x[0] * inv8, x[1] * inv8, x[2] * inv8, x[3] * inv8);
             o8.y = pack_fp8x4(x[4] * inv8, x[5] * inv8, x[6] * inv8, x[7] * inv8);
-            *reinterpret_cast<uint2*>(c8 + s * DA2_DPAD + cc * 8) = o8;
-            if (tz == 0) {      // Q only: its bf16 decode is the QK^T operand of the fp8 phase
+            if (tz == 1) *reinterpret_cast<uint2*>(c8 + s * DA2_DPAD + cc * 8) = o8;
+            if (tz == 0) {      // Q: its bf16 decode is the QK^T operand of the fp8 phase
                 uint4 ob;
                 ob.x = fp8x2_to_bf16x2<false>(o8.x);
                 ob.y = fp8x2_to_bf16x2<true>(o8.x);

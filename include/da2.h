@@ -84,9 +84,10 @@ typedef struct da2_plan_s da2_plan_t;
 /* Workspace sections (byte offsets from the workspace base, each 256-byte
  * aligned). BH = batch * heads, NB = n_blocks, T = DA2_TILE, P = DA2_DPAD.
  *   pool    f64 [4][BH][NB][P]  mean Q, max Q, mean K, max K over the window's tokens
- *   q8, k8  u8  [BH][NB][T][P]  E4M3 codes, slot-major
+ *   k8      u8  [BH][NB][T][P]  E4M3 codes of K, slot-major
  *   qb      bf16 [BH][NB][T][P] the Q E4M3 codes decoded to bf16 (exact, without the
- *                               block scale): the Q operand of the fp8 phase's QK^T
+ *                               block scale): the Q operand of the fp8 phase's QK^T;
+ *                               the decode is one-to-one, so it stands for the codes
  *   v8t     u8  [BH][NB][P][T]  E4M3 codes of V, channel-major (transposed tile)
  *   e8      u8  [3][BH][NB]     E8M0 scale of each block for q, k, v
  *   q4, k4  u8  [BH][NB][T][P/2] E2M1 codes, two per byte, low nibble = even channel
@@ -115,7 +116,7 @@ typedef struct da2_plan_info_s {
     int64_t slots;            /* n_blocks * block_size */
     double tau;
     uint64_t workspace_bytes;
-    uint64_t off_pool, off_q8, off_k8, off_v8t, off_e8;
+    uint64_t off_pool, off_k8, off_v8t, off_e8;
     uint64_t off_q4, off_k4, off_v4t, off_sq4, off_sk4, off_sv4t;
     uint64_t off_scores, off_labels, off_hi, off_lo, off_status;
     uint64_t off_qb, off_bias;
