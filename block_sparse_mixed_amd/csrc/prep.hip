@@ -5,12 +5,14 @@
 // max) for the draft map. [DraftAttention (arXiv 2505.14708), abstract]: Q, K
 // and V are reordered so that every 2D window is one contiguous tile.
 //
-// One workgroup per (block, batch*head, tensor). It reads the window's bf16
-// rows once (8 rows of 16 consecutive raster tokens for an 8x16 window),
-// stages them in LDS and writes:
+// One workgroup per four consecutive blocks of one (batch*head, tensor), the
+// next block's loads in flight while the current one is processed. It reads
+// each window's bf16 rows once (8 rows of 16 consecutive raster tokens for an
+// 8x16 window), stages them in LDS and writes:
 //   - E4M3 codes with one power-of-two scale for the whole block
-//     (Q, K slot-major; V channel-major so that PV can contract over slots),
-//     and for Q and K the same codes decoded to bf16 (scale-free, exact),
+//     (K slot-major; V channel-major so that PV can contract over slots),
+//     and for Q the same codes decoded to bf16 (scale-free, exact; the codes
+//     themselves are not stored),
 //   - MXFP4 codes with an E8M0 scale per 32 elements along the contraction
 //     axis (Q, K along channels; V along slots),
 //   - for Q and K, the per-channel mean (fp64, exact sum of bf16 values then
@@ -31,6 +33,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPitch = DA2_DPAD + 8;   // bf16 elements per LDS row (272 bytes)
+constexpr int kTilesPerGroup = 4;
 
 __device__ __forceinline__ uint32_t abs_bits(uint32_t bf16) { return bf16 & 0x7FFFu; }
 
@@ -38,37 +41,59 @@ __device__ __forceinline__ uint32_t abs_bits(uint32_t bf16) { return bf16 & 0x7F
 
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
     const Geo& g = a.g;
-    const int blk = blockIdx.x;
     const int bh = blockIdx.y;
     const int tz = blockIdx.z;                 // 0 = q, 1 = k, 2 = v
     const int tid = threadIdx.x;
     const int b = bh / g.heads;
     const int h = bh - b * g.heads;
-    const BlockPos pos = block_pos(g, blk);
 
     __shared__ __align__(16) uint16_t tile[DA2_TILE * kPitch];
     __shared__ uint32_t red[kThreads / 64];
     __shared__ double psum[DA2_DPAD];
     __shared__ float pmax[DA2_DPAD];
-    __shared__ int sraster[DA2_TILE];          // raster index of each slot, -1 for padding
+    __shared__ int sraster[2][DA2_TILE];       // raster index of each slot, -1 for padding (two tiles)
 
     const uint16_t* src = a.src[tz] + (int64_t)b * g.stride_b + (int64_t)h * g.stride_h;
-    // the window geometry once per slot (one integer division each), not per use
-    if (tid < DA2_TILE) sraster[tid] = (int)slot_raster(g, pos, tid);
+    // chunk ci = 8 channels of one slot; 16 chunks per slot row
+    auto load = [&](uint4 (&chunk)[8], const int* sr) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int ci = tid + kThreads * it;
+            const int s = ci >> 4;
+            const int cc = ci & 15;
+            const int64_t n = sr[s];
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (n >= 0 && cc * 8 < g.head_dim) v = *reinterpret_cast<const uint4*>(src + n * g.stride_n + cc * 8);
+            chunk[it] = v;
+        }
+    };
+    // A workgroup prepares kTilesPerGroup consecutive blocks; the loads of
+    // the next block are issued before the current one is processed, so
+    // that one tile's memory latency hides behind the other's work. The
+    // window geometry is tabulated once per slot (one integer division
+    // each), not per use.
+    const int blk0 = blockIdx.x * kTilesPerGroup;
+    if (tid < DA2_TILE) sraster[0][tid] = (int)slot_raster(g, block_pos(g, blk0), tid);
     __syncthreads();
-
-    // ---- load: chunk ci = 8 channels of one slot; 16 chunks per slot row ----
     uint4 chunk[8];
+    load(chunk, sraster[0]);
+#pragma unroll
+    for (int t = 0; t < kTilesPerGroup; ++t) {
+    const int blk = blk0 + t;
+    if (blk >= g.n_blocks) break;
+    const BlockPos pos = block_pos(g, blk);
+    const int* sr = sraster[t & 1];
+    const bool more = t + 1 < kTilesPerGroup && blk + 1 < g.n_blocks;
+    if (more && tid < DA2_TILE) sraster[(t + 1) & 1][tid] = (int)slot_raster(g, block_pos(g, blk + 1), tid);
+
+    // ---- stage the tile in LDS ----
     uint32_t amax_bits = 0;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
         const int ci = tid + kThreads * it;
         const int s = ci >> 4;
         const int cc = ci & 15;
-        const int64_t n = sraster[s];
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (n >= 0 && cc * 8 < g.head_dim) v = *reinterpret_cast<const uint4*>(src + n * g.stride_n + cc * 8);
-        chunk[it] = v;
+        const uint4 v = chunk[it];
         *reinterpret_cast<uint4*>(&tile[s * kPitch + cc * 8]) = v;
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -81,6 +106,10 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
     if ((tid & 63) == 0) red[tid >> 6] = amax_bits;
     __syncthreads();
     amax_bits = max(max(red[0], red[1]), max(red[2], red[3]));
+    // the next tile's loads go out now, into the registers this tile no
+    // longer needs (its raster table is visible after the barrier); this
+    // tile is read from LDS from here on
+    if (more) load(chunk, sraster[(t + 1) & 1]);
     const int e8 = fp8_exponent(bf16_bits_to_f32(amax_bits));
     const float inv8 = exp2i(-e8);
 
@@ -104,7 +133,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
             const int ci = tid + kThreads * it;
             const int s = ci >> 4;
             const int cc = ci & 15;
-            const uint32_t w[4] = {chunk[it].x, chunk[it].y, chunk[it].z, chunk[it].w};
+            const uint4 v = *reinterpret_cast<const uint4*>(&tile[s * kPitch + cc * 8]);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
             float x[8];
             uint32_t gmax = 0;
 #pragma unroll
@@ -193,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
         for (int s = half * 64; s < half * 64 + 64; ++s) {
             const float x = bf16_bits_to_f32(tile[s * kPitch + c]);
             sum4[s & 3] += (double)x;
-            mx4[s & 3] = sraster[s] >= 0 ? fmaxf(mx4[s & 3], x) : mx4[s & 3];
+            mx4[s & 3] = sr[s] >= 0 ? fmaxf(mx4[s & 3], x) : mx4[s & 3];
         }
         double sum = (sum4[0] + sum4[1]) + (sum4[2] + sum4[3]);
         float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
@@ -214,6 +244,9 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
             pool[(2 * tz + 1) * plane + tileid * DA2_DPAD + c] = maxv;
         }
     }
+    // the tile, the reduction slots and this tile's raster table are reused
+    __syncthreads();
+    }
 }
 
 hipError_t launch_prep(const Geo& g, const Layout& L, const void* q, const void* k, const void* v,
@@ -225,7 +258,8 @@ hipError_t launch_prep(const Geo& g, const Layout& L, const void* q, const void*
     a.src[2] = static_cast<const uint16_t*>(v);
     a.ws = static_cast<uint8_t*>(ws);
     a.L = L;
-    return launch_kernel(prep_kernel, dim3(g.n_blocks, g.bh, 3), dim3(kThreads), 0, stream, a);
+    return launch_kernel(prep_kernel, dim3((g.n_blocks + kTilesPerGroup - 1) / kTilesPerGroup, g.bh, 3), dim3(kThreads), 0,
+                         stream, a);
 }
 
 }  // namespace da2
