@@ -17,7 +17,8 @@
 //     axis (Q, K along channels; V along slots),
 //   - for Q and K, the per-channel mean (fp64, exact sum of bf16 values then
 //     one rounding) and maximum over the window's real tokens.
-// HBM-bound: ~2 bytes read and ~1.6 bytes written per element.
+// HBM-bound: ~2 bytes read and ~2.4 bytes written per element (the codes of
+// padded slots included).
 #include "common.hpp"
 
 namespace da2 {
