@@ -135,3 +135,12 @@ def test_prepare_large_block_counts(da2, grid):
     run = GpuRun(da2, w)
     say(f"check prepare {w.name} nb={run.nb}")
     check_prepare(run, 0, run.oracle_head(0))
+
+
+def test_attention_long_tile_lists(da2):
+    # 1089 blocks of 4 tokens, 327 retained per query block (109 fp8, 218
+    # MXFP4): long tile lists whose tiles are 124/128 padding, end to end on
+    # sampled query blocks
+    w = dataclasses.replace(S.TINY, name="blocks66", frames=1, grid_h=66, grid_w=66, win_h=2, win_w=2,
+                            head_dim=64, budget_hi=0.1, budget_lo=0.2)
+    _full_parity(da2, w, heads=[0], att_blocks=[0, 17, 544, 1088])
