@@ -47,14 +47,30 @@ __global__ __launch_bounds__(256) void draft_logits_kernel(Geo g, const double* 
     // Q and 4 tx .. 4 tx + 3 of K as two 16-byte reads each
     __shared__ __align__(16) double qs[kKc][kTile + 2];
     __shared__ __align__(16) double ks[kKc][kTile + 2];
-    double acc[4][4] = {};
-    for (int c0 = 0; c0 < g.head_dim; c0 += kKc) {
-        for (int e = tid; e < kTile * kKc; e += 256) {
+    // the next channel chunk is read into registers while this one is used
+    constexpr int kPer = kTile * kKc / 256;
+    double qn[kPer], kn[kPer];
+    auto gload = [&](int c0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            const int e = tid + 256 * t;
             const int r = e / kKc, cc = e % kKc;
-            qs[cc][r] = (i0 + r < nb) ? qp[(uint64_t)(i0 + r) * DA2_DPAD + c0 + cc] : 0.0;
-            ks[cc][r] = (j0 + r < nb) ? kp[(uint64_t)(j0 + r) * DA2_DPAD + c0 + cc] : 0.0;
+            qn[t] = (i0 + r < nb) ? qp[(uint64_t)(i0 + r) * DA2_DPAD + c0 + cc] : 0.0;
+            kn[t] = (j0 + r < nb) ? kp[(uint64_t)(j0 + r) * DA2_DPAD + c0 + cc] : 0.0;
+        }
+    };
+    double acc[4][4] = {};
+    gload(0);
+    for (int c0 = 0; c0 < g.head_dim; c0 += kKc) {
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            const int e = tid + 256 * t;
+            const int r = e / kKc, cc = e % kKc;
+            qs[cc][r] = qn[t];
+            ks[cc][r] = kn[t];
         }
         __syncthreads();
+        if (c0 + kKc < g.head_dim) gload(c0 + kKc);
 #pragma unroll 4
         for (int cc = 0; cc < kKc; ++cc) {
             const double2 q01 = *reinterpret_cast<const double2*>(&qs[cc][4 * ty]);
