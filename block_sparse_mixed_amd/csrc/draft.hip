@@ -96,14 +96,54 @@ __global__ __launch_bounds__(256) void draft_logits_kernel(Geo g, const double* 
         }
 }
 
+// The value of lane l ^ D (D < 64, a power of two) without a trip through
+// LDS for most D: quad permutes for 1 and 2, a row rotation for 8 (rows of
+// 16 lanes), the 16- and 32-lane swaps for 16 and 32, and a swizzle for 4.
+template <int D>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+    const int lane = threadIdx.x & 63;
+    if constexpr (D == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+    } else if constexpr (D == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+    } else if constexpr (D == 4) {
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, (4 << 10) | 0x1F);      // xor 4 within 32 lanes
+    } else if constexpr (D == 8) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);   // row_ror:8
+    } else if constexpr (D == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane & 16) ? r[0] : r[1];
+    } else {
+        static_assert(D == 32, "lane distance");
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane & 32) ? r[0] : r[1];
+    }
+}
+template <int D>
+__device__ __forceinline__ double lane_xor(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = lane_xor<D>((uint32_t)u), hi = lane_xor<D>((uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, lo | (hi << 32));
+}
+
 // Workgroup (four waves) maximum and sum of two values at once; each value
 // is reduced exactly as a reduction of its own would (butterfly within the
 // wave, then the four wave results in a fixed order).
+template <int D>
+__device__ __forceinline__ void butterfly_max2(double& a, double& b) {
+    a = fmax(a, lane_xor<D>(a));
+    b = fmax(b, lane_xor<D>(b));
+    if constexpr (D > 1) butterfly_max2<D / 2>(a, b);
+}
+template <int D>
+__device__ __forceinline__ void butterfly_sum2(double& a, double& b) {
+    a += lane_xor<D>(a);
+    b += lane_xor<D>(b);
+    if constexpr (D > 1) butterfly_sum2<D / 2>(a, b);
+}
+
 __device__ __forceinline__ void block_reduce_max2(double& a, double& b, double* red) {
-    for (int off = 32; off > 0; off >>= 1) {
-        a = fmax(a, __shfl_xor(a, off));
-        b = fmax(b, __shfl_xor(b, off));
-    }
+    butterfly_max2<32>(a, b);
     const int w = threadIdx.x >> 6;
     __syncthreads();
     if ((threadIdx.x & 63) == 0) {
@@ -116,10 +156,7 @@ __device__ __forceinline__ void block_reduce_max2(double& a, double& b, double* 
 }
 
 __device__ __forceinline__ void block_reduce_sum2(double& a, double& b, double* red) {
-    for (int off = 32; off > 0; off >>= 1) {
-        a += __shfl_xor(a, off);
-        b += __shfl_xor(b, off);
-    }
+    butterfly_sum2<32>(a, b);
     const int w = threadIdx.x >> 6;
     __syncthreads();
     if ((threadIdx.x & 63) == 0) {
@@ -166,7 +203,8 @@ struct SortState {
 // One compare-exchange step of stage k, partner distance jj: element e ends
 // up holding the first of the pair (e, e ^ jj) when it is the lower element
 // of an ascending pair or the upper element of a descending one.
-template <int R>
+// D: the lane distance jj / R when it is known at compile time (0 otherwise)
+template <int R, int D = 0>
 __device__ __forceinline__ void bitonic_step(SortState<R>& st, double* val, int32_t* idx, int base, int k, int jj) {
     if (jj < R) {
 #pragma unroll
@@ -190,8 +228,13 @@ __device__ __forceinline__ void bitonic_step(SortState<R>& st, double* val, int3
         const int d = jj / R;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            pv[r] = __shfl_xor(st.v[r], d);
-            pi[r] = __shfl_xor(st.ix[r], d);
+            if constexpr (D > 0) {
+                pv[r] = lane_xor<D>(st.v[r]);
+                pi[r] = (int)lane_xor<D>((uint32_t)st.ix[r]);
+            } else {
+                pv[r] = __shfl_xor(st.v[r], d);
+                pi[r] = __shfl_xor(st.ix[r], d);
+            }
         }
     } else {
         __syncthreads();
@@ -222,7 +265,7 @@ __device__ __forceinline__ void bitonic_step(SortState<R>& st, double* val, int3
 template <int R, int K, int JJ>
 __device__ __forceinline__ void bitonic_stages(SortState<R>& st, double* val, int32_t* idx, int base) {
     if constexpr (K <= 256 * R) {
-        bitonic_step<R>(st, val, idx, base, K, JJ);
+        bitonic_step<R, (JJ >= R && JJ < 64 * R) ? JJ / R : 0>(st, val, idx, base, K, JJ);
         if constexpr (JJ > 1)
             bitonic_stages<R, K, JJ / 2>(st, val, idx, base);
         else
