@@ -61,6 +61,8 @@ def parse():
                     help="budget sweep on the Wan-480p shape: time and error vs dense fp32 per point")
     ap.add_argument("--sweep-rows", type=int, default=2048,
                     help="query rows per head sampled for the error against dense attention")
+    ap.add_argument("--sweep-blocks", type=int, default=16,
+                    help="whole query blocks per head sampled for the error split and draft fidelity")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a streaming kernel of known size (read 1 GiB, write 1 GiB), for counter scaling")
     return ap.parse_args()
@@ -177,6 +179,87 @@ def dense_error(q, k, v, out, tau, rows_per_head, seed=0):
             "rows_per_head": int(rows.numel())}
 
 
+def token_blocks(w, info, device):
+    """Block (window) of every raster token: windows are numbered (frame,
+    window row, window column) row-major over whole windows per frame."""
+    import torch
+    t = torch.arange(w.tokens, device=device)
+    x = t % w.grid_w
+    y = (t // w.grid_w) % w.grid_h
+    f = t // (w.grid_w * w.grid_h)
+    return (f * info.n_wy + y // w.win_h) * info.n_wx + x // w.win_w
+
+
+def fidelity(w, info, q, k, v, out, labels, scores, blocks_per_head, seed=0, blocks=None):
+    """Error split and draft fidelity on a seeded sample of whole query blocks
+    of every head, in fp32 against exact attention over the same bf16 inputs.
+
+    Per sampled query block: dense attention (all keys), exact sparse
+    attention (softmax over the retained blocks' keys only), and the true
+    block mass M[i, j] (mean over block i's tokens of the dense probability
+    on block j's keys). Reported: relative L2 over the sampled rows of
+    sparse - dense (sparsification), out - sparse and out - dense (both over
+    the dense norm); the mean over query blocks of the true mass on the hi,
+    the lo and all retained blocks, and of the retained mass over the most
+    any selection of that size keeps (recall); and the relative Frobenius
+    distance between the draft scores C and M.
+
+    labels: int8 [B*H, nb, nb] (device); scores: [B*H, nb, nb] draft scores C;
+    blocks: the query blocks to sample (default: a seeded choice).
+    """
+    import torch
+    B, H, N, d = q.shape
+    nb = info.n_blocks
+    dev = q.device
+    tb = token_blocks(w, info, dev)
+    if blocks is None:
+        g = torch.Generator(device="cpu").manual_seed(seed)
+        blocks = torch.randperm(nb, generator=g)[:blocks_per_head]
+    blocks = torch.as_tensor(blocks).sort().values.to(dev)
+    rows = torch.nonzero(torch.isin(tb, blocks)).flatten()
+    pos = torch.searchsorted(blocks, tb[rows])                 # sampled-block slot of each row
+    cnt = torch.zeros(len(blocks), device=dev).index_add_(0, pos, torch.ones(len(rows), device=dev))
+    acc = dict(dense=0.0, sparse=0.0, q=0.0, total=0.0, cm=0.0, m=0.0)
+    hi_m, lo_m, ret_m, rec = [], [], [], []
+    for b in range(B):
+        for h in range(H):
+            bh = b * H + h
+            kk, vv = k[b, h].float(), v[b, h].float()
+            logits = (q[b, h, rows].float() @ kk.t()) * info.tau
+            p = torch.softmax(logits, dim=-1)
+            dense = p @ vv
+            lab = labels[bh].to(dev)[blocks].long()            # [nS, nb]
+            keep = lab[pos][:, tb] != 0                        # [R, N]
+            sparse = torch.softmax(logits.masked_fill(~keep, float("-inf")), dim=-1) @ vv
+            del logits, keep
+            got = out[b, h, rows].float()
+            acc["dense"] += float((dense * dense).sum())
+            acc["sparse"] += float(((sparse - dense) ** 2).sum())
+            acc["q"] += float(((got - sparse) ** 2).sum())
+            acc["total"] += float(((got - dense) ** 2).sum())
+            mrow = torch.zeros(len(rows), nb, device=dev).index_add_(1, tb, p)
+            del p
+            M = torch.zeros(len(blocks), nb, device=dev).index_add_(0, pos, mrow) / cnt[:, None]
+            C = scores[bh].to(dev)[blocks].float()
+            acc["cm"] += float(((C - M) ** 2).sum())
+            acc["m"] += float((M * M).sum())
+            n_ret = (lab != 0).sum(dim=1)
+            best = torch.sort(M, dim=1, descending=True).values.cumsum(dim=1).gather(1, (n_ret - 1)[:, None])[:, 0]
+            hi = (M * (lab == 2)).sum(dim=1)
+            lo = (M * (lab == 1)).sum(dim=1)
+            hi_m.append(hi)
+            lo_m.append(lo)
+            ret_m.append(hi + lo)
+            rec.append((hi + lo) / best)
+    mean = lambda xs: float(torch.cat(xs).mean())
+    return {"sparsification_rel_l2": (acc["sparse"] / acc["dense"]) ** 0.5,
+            "quantization_rel_l2": (acc["q"] / acc["dense"]) ** 0.5,
+            "total_rel_l2": (acc["total"] / acc["dense"]) ** 0.5,
+            "hi_mass": mean(hi_m), "lo_mass": mean(lo_m), "retained_mass": mean(ret_m),
+            "recall": mean(rec), "draft_map_rel_fro": (acc["cm"] / acc["m"]) ** 0.5,
+            "blocks_per_head": int(len(blocks)), "rows_per_head": int(len(rows))}
+
+
 def sweep(args):
     import torch
 
@@ -211,12 +294,16 @@ def sweep(args):
         dense, f_hi, f_lo = flops(w, info.n_blocks, info.n_hi, info.n_lo)
         t_star = f_hi / P_FP8 + f_lo / P_FP4
         err = dense_error(q, k, v, out, info.tau, args.sweep_rows)
+        BH, nb = w.batch * w.heads, info.n_blocks
+        labels = da2.workspace_section(plan, ws, "labels", torch.int8, (BH, nb, nb))
+        scores = da2.workspace_section(plan, ws, "scores", torch.float64, (2, BH, nb, nb))[0]
+        fid = fidelity(w, info, q, k, v, out, labels, scores, args.sweep_blocks)
         print(json.dumps({"sweep_point": {"budget_hi": hi, "budget_lo": lo, "n_hi": info.n_hi, "n_lo": info.n_lo},
                           "attention_ms": attn_ms, "prepare_ms": prep_ms,
                           "dense_equiv_tflops": dense / ((attn_ms + prep_ms) / 1e3) / 1e12,
                           "attention_executed_tflops": (f_hi + f_lo) / (attn_ms / 1e3) / 1e12,
                           "blended_roofline_frac": t_star / (attn_ms / 1e3) if f_hi + f_lo > 0 else None,
-                          "error_vs_dense_fp32": err, "workload": base.name}), flush=True)
+                          "error_vs_dense_fp32": err, "fidelity": fid, "workload": base.name}), flush=True)
         del ws, out, plan
 
 
