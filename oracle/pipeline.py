@@ -42,7 +42,8 @@ class HeadState:
 
 def prepare_head(cfg, q: np.ndarray, k: np.ndarray, v: np.ndarray) -> HeadState:
     """q, k, v [N, d] float64 of one (batch, head)."""
-    geo = Geometry(cfg.frames, cfg.grid_h, cfg.grid_w, cfg.win_h, cfg.win_w)
+    geo = Geometry(cfg.frames, cfg.grid_h, cfg.grid_w, cfg.win_h, cfg.win_w,
+                   pack_edges=bool(getattr(cfg, "pack_edges", False)))
     idx = geo.raster_index()
     valid = idx >= 0
     qb, kb, vb = (gather_blocks(t, idx) for t in (q, k, v))

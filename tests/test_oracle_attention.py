@@ -84,8 +84,10 @@ def _masked_sdpa(q, k, v, tau, mask):
     return out[0, 0].numpy()
 
 
-def test_unquantized_all_high_equals_dense_sdpa():
+@pytest.mark.parametrize("pack", [False, True])
+def test_unquantized_all_high_equals_dense_sdpa(pack):
     cfg = _cfg(frames=2, gh=9, gw=10, hi=1.0, lo=0.0)
+    cfg.pack_edges = pack
     q, k, v = _qkv(cfg, seed=2)
     st = P.prepare_head(cfg, q, k, v)
     assert np.all(st.labels == D.HI)
@@ -95,8 +97,10 @@ def test_unquantized_all_high_equals_dense_sdpa():
     np.testing.assert_allclose(P.dense_attention(q, k, v, st.tau), ref, rtol=0, atol=1e-12)
 
 
-def test_unquantized_sparse_equals_block_masked_sdpa():
+@pytest.mark.parametrize("pack", [False, True])
+def test_unquantized_sparse_equals_block_masked_sdpa(pack):
     cfg = _cfg(frames=2, gh=9, gw=10, hi=0.2, lo=0.3)
+    cfg.pack_edges = pack
     q, k, v = _qkv(cfg, seed=3)
     st = P.prepare_head(cfg, q, k, v)
     n = q.shape[0]

@@ -37,6 +37,45 @@ def test_geometry_landmarks_wan():
     assert idx[4 * 4, 0] == 30 * 52                                     # first window of frame 1
 
 
+@pytest.mark.parametrize("shape,expect", [
+    ((2, 16, 16, 4, 4), (32, 32)),          # Tiny: divisible, no edge stream
+    ((5, 32, 32, 8, 16), (40, 40)),         # Small: divisible
+    ((21, 30, 52, 8, 16), (256, 189)),      # Wan-480p shape: 9 full windows a frame + 67 stream blocks
+    ((33, 45, 80, 8, 16), (929, 825)),      # Hunyuan-720p shape: 25 a frame + 104
+    ((3, 5, 7, 4, 4), (7, 3)),              # ragged both ways, small
+    ((2, 3, 5, 4, 8), (1, 0)),              # grid smaller than a window: stream only
+])
+def test_packed_geometry_counts_and_bijection(shape, expect):
+    g = Geometry(*shape, pack_edges=True)
+    idx = g.raster_index()
+    assert (g.n_blocks, g.n_full) == expect
+    assert g.n_blocks == -(-g.tokens // g.block_size)          # no block wasted
+    real = idx[idx >= 0]
+    assert np.array_equal(np.sort(real), np.arange(g.tokens))
+    valid = idx >= 0
+    assert valid[:-1].all()                                     # only the last block may be short
+    assert valid[-1].sum() == g.tokens - (g.n_blocks - 1) * g.block_size
+    # the full windows are the padded geometry's full windows, in order
+    p = Geometry(*shape)
+    pidx = p.raster_index()
+    full = pidx[(pidx >= 0).all(axis=1)]
+    assert np.array_equal(idx[:g.n_full], full)
+    if shape[1] % shape[3] == 0 and shape[2] % shape[4] == 0:
+        assert np.array_equal(idx, pidx)
+
+
+def test_packed_geometry_landmarks_wan():
+    g = Geometry(21, 30, 52, 8, 16, pack_edges=True)
+    idx = g.raster_index()
+    assert idx[0, 0] == 0 and idx[1, 0] == 16 and idx[3, 0] == 8 * 52   # full windows (0,0) (0,1) (1,0)
+    assert idx[9, 0] == 30 * 52                                          # frame 1's first full window
+    e = idx[189]                                                         # first block of the edge stream:
+    assert e[0] == 48 and e[3] == 51 and e[4] == 52 + 48                 # window (0,3), 8 x 4 tokens
+    assert e[32] == 8 * 52 + 48 and e[64] == 16 * 52 + 48                # windows (1,3), (2,3)
+    assert e[96] == 24 * 52 and e[112] == 25 * 52                        # window (3,0): 6 x 16 tokens
+    assert idx[255, 119] == 32759 and (idx[255, 120:] == -1).all()       # frame 20's last corner token
+
+
 def _pool_torch(frame, ph, pw):
     """frame [H, W, d] -> avg/max over (ph, pw) windows with partial edge windows (ceil)."""
     x = torch.from_numpy(frame).permute(2, 0, 1)[None]
