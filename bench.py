@@ -32,6 +32,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan480p]
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -63,6 +64,10 @@ def parse():
                     help="query rows per head sampled for the error against dense attention")
     ap.add_argument("--sweep-blocks", type=int, default=16,
                     help="whole query blocks per head sampled for the error split and draft fidelity")
+    ap.add_argument("--pack-edges", action="store_true",
+                    help="packed edge windows (partial windows streamed into shared blocks) for the timed line and the sweep")
+    ap.add_argument("--no-alt-layout", action="store_true",
+                    help="do not also time the other block layout")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a streaming kernel of known size (read 1 GiB, write 1 GiB), for counter scaling")
     return ap.parse_args()
@@ -180,14 +185,33 @@ def dense_error(q, k, v, out, tau, rows_per_head, seed=0):
 
 
 def token_blocks(w, info, device):
-    """Block (window) of every raster token: windows are numbered (frame,
-    window row, window column) row-major over whole windows per frame."""
+    """Block of every raster token. Window layout: windows are numbered
+    (frame, window row, window column) row-major over whole windows per
+    frame. Packed edge windows (info.flags bit 0): the full windows are
+    numbered that way among themselves; then a frame's partial windows
+    (the right-hand column top to bottom, then the bottom row left to right,
+    row-major inside each) form a stream over all frames, cut into blocks of
+    win_h * win_w tokens."""
     import torch
     t = torch.arange(w.tokens, device=device)
     x = t % w.grid_w
     y = (t // w.grid_w) % w.grid_h
     f = t // (w.grid_w * w.grid_h)
-    return (f * info.n_wy + y // w.win_h) * info.n_wx + x // w.win_w
+    wy, wx = y // w.win_h, x // w.win_w
+    if not (info.flags & 1):
+        return (f * info.n_wy + wy) * info.n_wx + wx
+    bs = w.win_h * w.win_w
+    fwy, fwx = w.grid_h // w.win_h, w.grid_w // w.win_w
+    rem_h, rem_w = w.grid_h - fwy * w.win_h, w.grid_w - fwx * w.win_w
+    edge_frame = w.grid_h * w.grid_w - fwy * fwx * bs
+    full = (wy < fwy) & (wx < fwx)
+    right = fwy * w.win_h * rem_w
+    in_right = (wy < fwy) & (wx >= fwx)
+    pos_right = wy * w.win_h * rem_w + (y - wy * w.win_h) * rem_w + (x - fwx * w.win_w)
+    ww = torch.clamp(w.grid_w - wx * w.win_w, max=w.win_w)
+    pos_bottom = right + wx * rem_h * w.win_w + (y - fwy * w.win_h) * ww + (x - wx * w.win_w)
+    pos = f * edge_frame + torch.where(in_right, pos_right, pos_bottom)
+    return torch.where(full, (f * fwy + wy) * fwx + wx, info.n_full + pos // bs)
 
 
 def fidelity(w, info, q, k, v, out, labels, scores, blocks_per_head, seed=0, blocks=None):
@@ -267,10 +291,13 @@ def sweep(args):
     import synthetic as S
     base = S.WORKLOADS[args.workload]
     q, k, v = (t.to("cuda:0") for t in S.make_qkv(base))
+    if args.pack_edges:
+        base = dataclasses.replace(base, name=base.name + "-packed", pack_edges=True)
     for hi, lo in S.SWEEP_POINTS:
         w = S.with_budgets(base, hi, lo)
         cfg = da2.make_config(w.batch, w.heads, w.frames, w.grid_h, w.grid_w, w.head_dim, w.win_h, w.win_w,
-                              w.budget_hi, w.budget_lo, out_dtype=da2.DA2_OUT_FP32)
+                              w.budget_hi, w.budget_lo, out_dtype=da2.DA2_OUT_FP32,
+                              flags=da2.DA2_FLAG_PACK_EDGES if w.pack_edges else 0)
         plan = da2.da2_plan(cfg)
         info = plan.info
         ws = plan.workspace(q.device)
@@ -307,6 +334,48 @@ def sweep(args):
         del ws, out, plan
 
 
+def time_layout(w, qd, kd, vd, pack, steps, warmup):
+    """Plan the workload in one block layout and time `steps` whole steps
+    (prepare + attention) on the current stream with HIP events, after
+    `warmup` untimed ones. Returns the plan info, per-step prepare,
+    attention and step times (ms) and the wall time of the timed loop (s)."""
+    import torch
+
+    import block_sparse_mixed_amd as da2
+    cfg = da2.make_config(w.batch, w.heads, w.frames, w.grid_h, w.grid_w, w.head_dim, w.win_h, w.win_w,
+                          w.budget_hi, w.budget_lo, out_dtype=da2.DA2_OUT_BF16,
+                          flags=da2.DA2_FLAG_PACK_EDGES if pack else 0)
+    plan = da2.da2_plan(cfg)
+    ws = plan.workspace(qd.device)
+    out = torch.empty(w.batch, w.heads, w.tokens, w.head_dim, dtype=torch.bfloat16, device=qd.device)
+    stream = torch.cuda.current_stream(qd.device)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        da2.da2_prepare(plan, qd, kd, vd, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        da2.da2_attention(plan, ws, out, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prep_ms = [e[0].elapsed_time(e[1]) for e in events]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in events]
+    step_ms = [e[0].elapsed_time(e[2]) for e in events]
+    return plan.info, prep_ms, attn_ms, step_ms, wall
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -326,42 +395,26 @@ def main():
 
     w = S.WORKLOADS[args.workload]
     q, k, v = S.make_qkv(w)
+    if args.pack_edges:
+        w = dataclasses.replace(w, name=w.name + "-packed", pack_edges=True)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, args.cpu_sample_blocks)
     dev = torch.device("cuda:0")
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
-    cfg = da2.make_config(w.batch, w.heads, w.frames, w.grid_h, w.grid_w, w.head_dim, w.win_h, w.win_w,
-                          w.budget_hi, w.budget_lo, out_dtype=da2.DA2_OUT_BF16)
-    plan = da2.da2_plan(cfg)
-    info = plan.info
-    ws = plan.workspace(dev)
-    out = torch.empty(w.batch, w.heads, w.tokens, w.head_dim, dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        da2.da2_prepare(plan, qd, kd, vd, ws, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        da2.da2_attention(plan, ws, out, stream)
-        if ev is not None:
-            ev[2].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    prep_ms = [e[0].elapsed_time(e[1]) for e in events]
-    attn_ms = [e[1].elapsed_time(e[2]) for e in events]
-    step_ms = [e[0].elapsed_time(e[2]) for e in events]
+    info, prep_ms, attn_ms, step_ms, wall = time_layout(w, qd, kd, vd, args.pack_edges, args.steps, args.warmup)
+    alt = None
+    if not args.no_alt_layout:
+        a_info, a_prep, a_attn, a_step, _ = time_layout(w, qd, kd, vd, not args.pack_edges, args.steps, args.warmup)
+        a_dense, a_hi, a_lo = flops(w, a_info.n_blocks, a_info.n_hi, a_info.n_lo)
+        a_attn_s = sum(a_attn) / len(a_attn) / 1e3
+        a_step_s = sum(a_step) / len(a_step) / 1e3
+        alt = {"layout": "packed_edges" if not args.pack_edges else "padded_windows",
+               "n_blocks": a_info.n_blocks, "n_hi": a_info.n_hi, "n_lo": a_info.n_lo,
+               "attention_ms": a_attn_s * 1e3, "prepare_ms": sum(a_prep) / len(a_prep),
+               "step_ms_events": a_step_s * 1e3,
+               "dense_equiv_tflops_step_events": a_dense / a_step_s / 1e12,
+               "roofline_frac": (a_hi / P_FP8 + a_lo / P_FP4) / a_attn_s}
     ms_per_step = wall * 1e3 / args.steps
     dense, f_hi, f_lo = flops(w, info.n_blocks, info.n_hi, info.n_lo)
     t_star = f_hi / P_FP8 + f_lo / P_FP4
@@ -386,7 +439,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "frames": w.frames,
                    "grid": [w.grid_h, w.grid_w], "tokens": w.tokens, "head_dim": w.head_dim,
                    "window": [w.win_h, w.win_w], "budget_hi": w.budget_hi, "budget_lo": w.budget_lo,
-                   "n_blocks": info.n_blocks, "n_hi": info.n_hi, "n_lo": info.n_lo, "out_dtype": "bf16"},
+                   "n_blocks": info.n_blocks, "n_hi": info.n_hi, "n_lo": info.n_lo, "out_dtype": "bf16",
+                   "layout": "packed_edges" if args.pack_edges else "padded_windows"},
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": blended_peak / 1e12, "unit": "TFLOP/s",
                      "frac": achieved / blended_peak, "traffic": recorded_traffic(w.name)},
         "cpu_baseline": cpu,
@@ -399,6 +453,7 @@ def main():
         "blended_roofline_ms": t_star * 1e3,
         "issued_mix_roofline_ms": t_star_instr * 1e3,
         "flops": {"dense_equiv": dense, "f_hi": f_hi, "f_lo": f_lo},
+        "other_layout": alt,
     }
     print(json.dumps(res), flush=True)
 

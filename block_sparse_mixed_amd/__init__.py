@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libda2.so")
 
 DA2_OK, DA2_ERR_INVALID_ARG, DA2_ERR_UNSUPPORTED, DA2_ERR_WORKSPACE, DA2_ERR_HIP = range(5)
 DA2_OUT_BF16, DA2_OUT_FP32 = 0, 1
+DA2_FLAG_PACK_EDGES = 1
 DA2_SKIP, DA2_LO, DA2_HI = 0, 1, 2
 TILE = 128
 DPAD = 128
@@ -54,7 +55,7 @@ class PlanInfo(ctypes.Structure):
     ] + [(n, ctypes.c_uint64) for n in (
         "off_pool", "off_k8", "off_v8t", "off_e8", "off_q4", "off_k4", "off_v4t",
         "off_sq4", "off_sk4", "off_sv4t", "off_scores", "off_labels", "off_hi", "off_lo", "off_status",
-        "off_qb", "off_bias")]
+        "off_qb", "off_bias")] + [("n_full", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

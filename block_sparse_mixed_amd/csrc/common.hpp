@@ -27,37 +27,82 @@ hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t shm
         vals);
 }
 
-// Window (block) position of block index blk: (frame, window row, window column).
+// Position of block blk. Window layout: every block is one window, numbered
+// (frame, window row, window column). Packed layout: the full windows come
+// first, numbered the same way among themselves, then blocks cut from one
+// stream of the partial windows' tokens (window by window in (frame, window
+// row, window column) order, row-major inside each window); for those,
+// edge0 is the stream position of slot 0 (-1 for a window block).
 struct BlockPos {
     int t, wy, wx;
+    int edge0;
 };
 
-__device__ __forceinline__ BlockPos block_pos(const Geo& g, int blk) {
-    const int per_frame = g.n_wy * g.n_wx;
+__host__ __device__ __forceinline__ BlockPos block_pos(const Geo& g, int blk) {
     BlockPos p;
+    p.edge0 = -1;
+    if (g.pack && blk >= g.n_full) {
+        p.t = p.wy = p.wx = 0;
+        p.edge0 = (blk - g.n_full) * g.block_size;
+        return p;
+    }
+    const int nwy = g.pack ? g.fwy : g.n_wy;
+    const int nwx = g.pack ? g.fwx : g.n_wx;
+    const int per_frame = nwy * nwx;
     p.t = blk / per_frame;
     const int r = blk - p.t * per_frame;
-    p.wy = r / g.n_wx;
-    p.wx = r - p.wy * g.n_wx;
+    p.wy = r / nwx;
+    p.wx = r - p.wy * nwx;
     return p;
 }
 
 // Raster index of slot s of block p, or -1 for a padded slot. Slots are
-// row-major inside the window.
-__device__ __forceinline__ int64_t slot_raster(const Geo& g, const BlockPos& p, int s) {
+// row-major inside a window. In the packed stream, a frame's partial windows
+// are the right-hand column (window rows 0 .. fwy-1, rem_w columns wide)
+// followed by the bottom row (rem_h rows high, every window column).
+__host__ __device__ __forceinline__ int64_t slot_raster(const Geo& g, const BlockPos& p, int s) {
     if (s >= g.block_size) return -1;
-    const int iy = s / g.win_w;
-    const int ix = s - iy * g.win_w;
-    const int y = p.wy * g.win_h + iy;
-    const int x = p.wx * g.win_w + ix;
-    if (y >= g.grid_h || x >= g.grid_w) return -1;
-    return ((int64_t)p.t * g.grid_h + y) * g.grid_w + x;
+    int t, y, x;
+    if (p.edge0 >= 0) {
+        const int e = p.edge0 + s;
+        if (e >= g.edge_total) return -1;
+        t = e / g.edge_frame;
+        const int r = e - t * g.edge_frame;
+        const int rem_w = g.grid_w - g.fwx * g.win_w;
+        const int right = g.fwy * g.win_h * rem_w;          // tokens of the right-hand column
+        if (r < right) {                                     // (rem_w > 0 here)
+            const int wsz = g.win_h * rem_w;
+            const int wy = r / wsz;
+            const int r2 = r - wy * wsz;
+            const int iy = r2 / rem_w;
+            y = wy * g.win_h + iy;
+            x = g.fwx * g.win_w + (r2 - iy * rem_w);
+        } else {                                             // (rem_h > 0 here)
+            const int rem_h = g.grid_h - g.fwy * g.win_h;
+            const int r1 = r - right;
+            const int wx = r1 / (rem_h * g.win_w);
+            const int r2 = r1 - wx * rem_h * g.win_w;
+            const int ww = g.grid_w - wx * g.win_w < g.win_w ? g.grid_w - wx * g.win_w : g.win_w;
+            const int iy = r2 / ww;
+            y = g.fwy * g.win_h + iy;
+            x = wx * g.win_w + (r2 - iy * ww);
+        }
+    } else {
+        const int iy = s / g.win_w;
+        const int ix = s - iy * g.win_w;
+        t = p.t;
+        y = p.wy * g.win_h + iy;
+        x = p.wx * g.win_w + ix;
+        if (y >= g.grid_h || x >= g.grid_w) return -1;
+    }
+    return ((int64_t)t * g.grid_h + y) * g.grid_w + x;
 }
 
 // Number of real tokens in block p.
-__device__ __forceinline__ int block_count(const Geo& g, const BlockPos& p) {
-    const int rows = min(g.win_h, g.grid_h - p.wy * g.win_h);
-    const int cols = min(g.win_w, g.grid_w - p.wx * g.win_w);
+__host__ __device__ __forceinline__ int block_count(const Geo& g, const BlockPos& p) {
+    if (p.edge0 >= 0) return g.edge_total - p.edge0 < g.block_size ? g.edge_total - p.edge0 : g.block_size;
+    const int rows = g.grid_h - p.wy * g.win_h < g.win_h ? g.grid_h - p.wy * g.win_h : g.win_h;
+    const int cols = g.grid_w - p.wx * g.win_w < g.win_w ? g.grid_w - p.wx * g.win_w : g.win_w;
     return rows * cols;
 }
 

@@ -11,6 +11,9 @@ namespace da2 {
 struct Geo {
     int32_t frames, grid_h, grid_w, win_h, win_w;
     int32_t n_wy, n_wx, n_blocks, block_size, head_dim, heads, bh;
+    // packed edge windows: pack != 0; fwy x fwx full windows a frame, n_full
+    // of them in all; edge_frame partial-window tokens a frame, edge_total in all
+    int32_t pack, fwy, fwx, n_full, edge_frame, edge_total;
     int32_t n_hi, n_lo;
     int64_t tokens;
     int64_t stride_b, stride_h, stride_n;

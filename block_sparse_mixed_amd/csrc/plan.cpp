@@ -20,7 +20,7 @@ extern "C" da2_status da2_plan(const da2_config* cfg, da2_plan_t** out) {
     if (c.batch <= 0 || c.heads <= 0 || c.frames <= 0 || c.grid_h <= 0 || c.grid_w <= 0 ||
         c.head_dim <= 0 || c.win_h <= 0 || c.win_w <= 0)
         return DA2_ERR_INVALID_ARG;
-    if (c.flags != 0) return DA2_ERR_INVALID_ARG;
+    if ((c.flags & ~(uint32_t)DA2_FLAG_PACK_EDGES) != 0) return DA2_ERR_INVALID_ARG;
     if (c.out_dtype != DA2_OUT_BF16 && c.out_dtype != DA2_OUT_FP32) return DA2_ERR_INVALID_ARG;
     if (!(c.budget_hi >= 0.0 && c.budget_hi <= 1.0 && c.budget_lo >= 0.0 && std::isfinite(c.budget_lo)))
         return DA2_ERR_INVALID_ARG;
@@ -37,10 +37,17 @@ extern "C" da2_status da2_plan(const da2_config* cfg, da2_plan_t** out) {
     g.win_w = c.win_w;
     g.n_wy = (c.grid_h + c.win_h - 1) / c.win_h;
     g.n_wx = (c.grid_w + c.win_w - 1) / c.win_w;
+    g.block_size = c.win_h * c.win_w;
     int64_t nb = (int64_t)c.frames * g.n_wy * g.n_wx;
     if (nb > DA2_MAX_BLOCKS) return DA2_ERR_UNSUPPORTED;
+    g.pack = (c.flags & DA2_FLAG_PACK_EDGES) ? 1 : 0;
+    g.fwy = c.grid_h / c.win_h;
+    g.fwx = c.grid_w / c.win_w;
+    g.n_full = (int32_t)((int64_t)c.frames * g.fwy * g.fwx);
+    g.edge_frame = c.grid_h * c.grid_w - g.fwy * g.fwx * g.block_size;
+    g.edge_total = (int32_t)((int64_t)c.frames * g.edge_frame);   // < the padded slot count, which fits
+    if (g.pack) nb = g.n_full + ((int64_t)g.edge_total + g.block_size - 1) / g.block_size;
     g.n_blocks = (int32_t)nb;
-    g.block_size = c.win_h * c.win_w;
     g.head_dim = c.head_dim;
     g.heads = c.heads;
     int64_t bh = (int64_t)c.batch * c.heads;
@@ -128,6 +135,8 @@ extern "C" da2_status da2_plan_info(const da2_plan_t* plan, da2_plan_info_t* out
     i.slots = (int64_t)g.n_blocks * g.block_size;
     i.tau = g.tau;
     i.workspace_bytes = L.total;
+    i.n_full = g.n_full;
+    i.flags = plan->cfg.flags;
     i.off_pool = L.pool;
     i.off_k8 = L.k8;
     i.off_v8t = L.v8t;

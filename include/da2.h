@@ -50,6 +50,18 @@ typedef enum da2_status {
 
 enum { DA2_OUT_BF16 = 0, DA2_OUT_FP32 = 1 };
 
+/* da2_config.flags.
+ * DA2_FLAG_PACK_EDGES: packed edge windows. The full windows stay one block
+ * each (numbered (frame, window row, window column) among themselves, first);
+ * the tokens of every partial window follow as one stream, window by window
+ * in (frame, window row, window column) order and row-major inside each
+ * window, cut into consecutive blocks of win_h * win_w tokens, so only the
+ * last block can be short. A stream block may mix windows and frames; its
+ * pooled statistics are over its own tokens. The pages fix neither this nor
+ * the default (partial windows padded up to whole blocks); packing removes
+ * the padded slots from the attention's work. */
+enum { DA2_FLAG_PACK_EDGES = 1u };
+
 /* Block labels, one int8 per (query block, key block). */
 enum { DA2_SKIP = 0, DA2_LO = 1, DA2_HI = 2 };
 
@@ -76,7 +88,7 @@ typedef struct da2_config {
     int64_t stride_h;         /* all three 0 selects the contiguous layout  */
     int64_t stride_n;
     int32_t out_dtype;        /* DA2_OUT_BF16 or DA2_OUT_FP32 */
-    uint32_t flags;           /* reserved, must be 0 */
+    uint32_t flags;           /* 0 or DA2_FLAG_PACK_EDGES; other bits are invalid */
 } da2_config;
 
 typedef struct da2_plan_s da2_plan_t;
@@ -120,12 +132,17 @@ typedef struct da2_plan_info_s {
     uint64_t off_q4, off_k4, off_v4t, off_sq4, off_sk4, off_sv4t;
     uint64_t off_scores, off_labels, off_hi, off_lo, off_status;
     uint64_t off_qb, off_bias;
+    int32_t n_full;           /* full windows (fill a block each); with DA2_FLAG_PACK_EDGES the
+                                 first n_full blocks, the rest being the packed stream */
+    uint32_t flags;           /* the configuration's flags */
 } da2_plan_info_t;
 
 /* Validate cfg and build a plan. Host only: touches no GPU state.
  * Geometry [DraftAttention (arXiv 2505.14708), abstract; news article on it,
  * method steps 1 and 4]: each frame is cut into win_h x win_w windows, padded
- * up to whole windows; a window is one block. Budget counts per query block
+ * up to whole windows; a window is one block (with DA2_FLAG_PACK_EDGES: the
+ * full windows plus ceil(partial-window tokens / (win_h * win_w)) packed
+ * blocks). Budget counts per query block
  * [DraftAttention2, abstract, configurable budgets]:
  *   n_hi = floor(budget_hi * NB + 1/2),
  *   n_ret = floor((budget_hi + min(budget_lo, 1 - budget_hi)) * NB + 1/2),

@@ -51,6 +51,7 @@ class Workload:
     outlier_scale: float = 8.0
     temporal_rho: float = 0.0
     seed: int = 0
+    pack_edges: bool = False           # packed edge windows (geometry only; inputs unchanged)
 
     @property
     def tokens(self) -> int:

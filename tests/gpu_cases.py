@@ -46,13 +46,14 @@ class GpuRun:
         self.q, self.k, self.v = (t.cuda() for t in (self.qc, self.kc, self.vc))
         cfg = da2.make_config(w.batch, w.heads, w.frames, w.grid_h, w.grid_w, w.head_dim, w.win_h, w.win_w,
                               w.budget_hi, w.budget_lo,
-                              out_dtype=da2.DA2_OUT_FP32 if out_fp32 else da2.DA2_OUT_BF16)
+                              out_dtype=da2.DA2_OUT_FP32 if out_fp32 else da2.DA2_OUT_BF16,
+                              flags=da2.DA2_FLAG_PACK_EDGES if w.pack_edges else 0)
         self.plan = da2.da2_plan(cfg)
         self.info = self.plan.info
         self.nb = self.info.n_blocks
         self.bh = w.batch * w.heads
         self.ws = self.plan.workspace()
-        say(f"da2_prepare {w.name} B={w.batch} H={w.heads} N={w.tokens} d={w.head_dim} nb={self.nb} "
+        say(f"da2_prepare {w.name} B={w.batch} H={w.heads} N={w.tokens} d={w.head_dim} nb={self.nb} pack={int(w.pack_edges)} "
             f"n_hi={self.info.n_hi} n_lo={self.info.n_lo}")
         da2.da2_prepare(self.plan, self.q, self.k, self.v, self.ws)
         torch.cuda.synchronize()

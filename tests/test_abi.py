@@ -50,6 +50,15 @@ def test_plan_wan_shape_matches_oracle_geometry_and_counts():
     assert i.tau == pytest.approx(1 / np.sqrt(128), rel=0, abs=0)
 
 
+def test_plan_packed_wan_shape():
+    p = da2.da2_plan(_cfg(flags=da2.DA2_FLAG_PACK_EDGES))
+    i = p.info
+    g = Geometry(21, 30, 52, 8, 16, pack_edges=True)
+    assert (i.n_blocks, i.n_full, i.flags) == (g.n_blocks, g.n_full, 1) == (256, 189, 1)
+    assert (i.n_hi, i.n_lo) == budget_counts(256, 0.15, 0.35) == (38, 90)
+    assert i.tokens == 32760 and i.slots == 32768
+
+
 def test_budget_counts_agree_with_oracle_on_many_configs():
     rng = np.random.default_rng(0)
     for _ in range(300):
@@ -57,18 +66,21 @@ def test_budget_counts_agree_with_oracle_on_many_configs():
         wh, ww = [(4, 4), (8, 16), (8, 8), (2, 16)][rng.integers(0, 4)]
         hi = float(rng.choice([0.0, 0.05, 0.1, 0.15, 0.25, 1 / 3, 0.5, 1.0, rng.random()]))
         lo = float(rng.choice([0.0, 0.2, 0.35, 0.4, 1.0, rng.random()]))
-        nb = Geometry(int(frames), int(gh), int(gw), wh, ww).n_blocks
+        pack = bool(rng.integers(0, 2))
+        nb = Geometry(int(frames), int(gh), int(gw), wh, ww, pack_edges=pack).n_blocks
+        flags = da2.DA2_FLAG_PACK_EDGES if pack else 0
         try:
             want = budget_counts(nb, hi, lo)
         except ValueError:
             with pytest.raises(da2.Da2Error) as e:
                 da2.da2_plan(_cfg(frames=int(frames), grid_h=int(gh), grid_w=int(gw), win_h=wh, win_w=ww,
-                                  budget_hi=hi, budget_lo=lo))
+                                  budget_hi=hi, budget_lo=lo, flags=flags))
             assert e.value.status == da2.DA2_ERR_INVALID_ARG
             continue
         p = da2.da2_plan(_cfg(frames=int(frames), grid_h=int(gh), grid_w=int(gw), win_h=wh, win_w=ww,
-                              budget_hi=hi, budget_lo=lo))
+                              budget_hi=hi, budget_lo=lo, flags=flags))
         assert (p.info.n_blocks, p.info.n_hi, p.info.n_lo) == (nb, *want)
+        assert p.info.flags == flags and p.info.n_full == Geometry(int(frames), int(gh), int(gw), wh, ww).n_full
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -80,7 +92,8 @@ def test_budget_counts_agree_with_oracle_on_many_configs():
     (dict(budget_hi=1.5), da2.DA2_ERR_INVALID_ARG),
     (dict(budget_hi=0.0, budget_lo=0.0), da2.DA2_ERR_INVALID_ARG),
     (dict(out_dtype=7), da2.DA2_ERR_INVALID_ARG),
-    (dict(flags=1), da2.DA2_ERR_INVALID_ARG),
+    (dict(flags=2), da2.DA2_ERR_INVALID_ARG),
+    (dict(flags=3), da2.DA2_ERR_INVALID_ARG),
     (dict(frames=200, grid_h=64, grid_w=64), da2.DA2_ERR_UNSUPPORTED),
 ])
 def test_plan_rejects(kw, status):

@@ -144,3 +144,24 @@ def test_attention_long_tile_lists(da2):
     w = dataclasses.replace(S.TINY, name="blocks66", frames=1, grid_h=66, grid_w=66, win_h=2, win_w=2,
                             head_dim=64, budget_hi=0.1, budget_lo=0.2)
     _full_parity(da2, w, heads=[0], att_blocks=[0, 17, 544, 1088])
+
+
+def test_packed_edges_full(da2):
+    # packed edge windows: stream blocks mixing windows and frames, a short
+    # last block; 128-token windows with d = 128, and 16-token windows
+    cases = [
+        dataclasses.replace(S.WAN480, name="packed-3f", heads=2, frames=3, pack_edges=True),
+        dataclasses.replace(S.TINY, name="packed-small-win", frames=2, grid_h=10, grid_w=9, win_h=4, win_w=4,
+                            budget_hi=0.25, budget_lo=0.25, pack_edges=True),
+        dataclasses.replace(S.TINY, name="packed-subwindow", frames=2, grid_h=5, grid_w=7, win_h=8, win_w=16,
+                            budget_hi=1.0, budget_lo=0.0, pack_edges=True),
+    ]
+    for w in cases:
+        _full_parity(da2, w)
+
+
+def test_wan_shape_packed_sampled(da2):
+    # full-size packed launch: 189 full windows + 67 stream blocks (the last
+    # one 120 tokens); outputs on full-window, stream and last blocks
+    w = dataclasses.replace(S.WAN480, name="wan480p-packed", pack_edges=True)
+    _full_parity(da2, w, heads=[0, 11], att_blocks=[0, 188, 189, 200, 255])

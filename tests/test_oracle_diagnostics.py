@@ -15,6 +15,7 @@ import pytest
 from oracle import diagnostics as X
 from oracle import draft as D
 from oracle import pipeline as P
+from oracle.geometry import Geometry
 
 
 def _cfg(frames=2, gh=8, gw=8, d=16, wh=4, ww=4, hi=0.25, lo=0.25):
@@ -129,7 +130,27 @@ def test_exact_attention_on_the_ideal_selection_beats_the_worst():
     assert best["sparsification"] < 0.5 * worst["sparsification"]
 
 
-def test_bench_fidelity_measure_matches_the_oracle():
+@pytest.mark.parametrize("shape", [(2, 16, 16, 4, 4), (21, 30, 52, 8, 16), (3, 5, 7, 4, 4), (2, 3, 5, 4, 8),
+                                   (4, 9, 10, 4, 4), (2, 11, 13, 2, 8), (2, 30, 52, 16, 8), (1, 17, 33, 8, 16)])
+@pytest.mark.parametrize("pack", [False, True])
+def test_bench_token_blocks_match_the_oracle_geometry(shape, pack):
+    import bench
+
+    g = Geometry(*shape, pack_edges=pack)
+    w = SimpleNamespace(frames=shape[0], grid_h=shape[1], grid_w=shape[2], win_h=shape[3], win_w=shape[4],
+                        tokens=g.tokens)
+    info = SimpleNamespace(n_wy=g.n_wy, n_wx=g.n_wx, n_full=g.n_full, flags=int(pack))
+    got = bench.token_blocks(w, info, "cpu").numpy()
+    idx = g.raster_index()
+    want = np.empty(g.tokens, dtype=np.int64)
+    for b in range(g.n_blocks):
+        want[idx[b][idx[b] >= 0]] = b
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("pack,blocks", [(False, [1, 4, 7, 13, 22, 29]),     # of 30 windows (2 x 5 x 3)
+                                         (True, [0, 5, 19, 20, 21, 22])])    # of 20 full + 3 stream blocks
+def test_bench_fidelity_measure_matches_the_oracle(pack, blocks):
     # the benchmark's fp32 torch measurement, fed the oracle's labels, scores
     # and output, reproduces the oracle's float64 diagnostics on the same
     # sampled query blocks (ragged windows, two heads)
@@ -138,12 +159,14 @@ def test_bench_fidelity_measure_matches_the_oracle():
     import bench
 
     cfg = _cfg(gh=10, gw=9, d=32, wh=2, ww=4, hi=0.1, lo=0.3)
+    cfg.pack_edges = pack
     w = SimpleNamespace(batch=1, heads=2, tokens=cfg.frames * cfg.grid_h * cfg.grid_w, **vars(cfg))
     heads = [_qkv(cfg, seed=10 + h) for h in range(2)]
     sts = [P.prepare_head(cfg, *qkv) for qkv in heads]
     geo = sts[0].geo
-    info = SimpleNamespace(n_blocks=geo.n_blocks, n_wy=geo.n_wy, n_wx=geo.n_wx, tau=sts[0].tau)
-    blocks = [1, 4, 7, 13, 22, 29]          # of 30 (2 frames x 5 x 3 windows)
+    info = SimpleNamespace(n_blocks=geo.n_blocks, n_wy=geo.n_wy, n_wx=geo.n_wx, tau=sts[0].tau,
+                           n_full=geo.n_full, flags=int(pack))
+    assert geo.n_blocks == (23 if pack else 30)
     outs = [X.error_split(st, *qkv) for st, qkv in zip(sts, heads)]
     t = lambda i: torch.from_numpy(np.stack([qkv[i] for qkv in heads]))[None].float()
     method = torch.from_numpy(np.stack([o["method"] for o in outs]))[None].float()
