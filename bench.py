@@ -18,7 +18,7 @@ FETCH_SIZE and WRITE_SIZE counters (rocprofv3 --pmc), each scaled by what the
 same counter reads for a plain streaming kernel of known size
 (`--copy-calibration`). Those figures are kept in
 profiles/attn_wan480p_traffic.md together with the SHA-256 of the attention
-kernel's source they were taken on; when the source has changed since, the
+kernel's sources (attn.hip, common.hpp) they were taken on; when the source has changed since, the
 field is null.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan480p]
@@ -73,13 +73,18 @@ def parse():
     return ap.parse_args()
 
 
-ATTN_SOURCE = os.path.join(HERE, "block_sparse_mixed_amd", "csrc", "attn.hip")
+# the attention kernel's sources: the kernel file and the geometry helpers it includes
+ATTN_SOURCES = [os.path.join(HERE, "block_sparse_mixed_amd", "csrc", f) for f in ("attn.hip", "common.hpp")]
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "attn_wan480p_traffic.md")
 
 
 def attn_source_sha256():
-    with open(ATTN_SOURCE, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()
+    """SHA-256 of the attention kernel's sources, concatenated in order."""
+    h = hashlib.sha256()
+    for path in ATTN_SOURCES:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def recorded_traffic(workload):
