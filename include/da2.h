@@ -156,7 +156,12 @@ void da2_plan_destroy(da2_plan_t* plan);
 /* Sizes, budget counts and workspace offsets of a plan. */
 da2_status da2_plan_info(const da2_plan_t* plan, da2_plan_info_t* out);
 
-/* Enqueue operand preparation and the draft ranking on hip_stream (a
+/* da2_prepare, da2_attention and da2_set_labels enqueue kernel launches
+ * only (no allocation, memset or copy), so a caller may capture them in a
+ * HIP graph; a replay reads and writes the buffers captured, with whatever
+ * values they hold at replay time.
+ *
+ * Enqueue operand preparation and the draft ranking on hip_stream (a
  * hipStream_t; NULL = the null stream). Asynchronous.
  * [DraftAttention2, abstract]: 2D average- and max-pooled Q and K give a
  * low-resolution draft attention map that scores every (query block, key
