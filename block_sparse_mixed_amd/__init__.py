@@ -203,17 +203,28 @@ def workspace_section(plan: Plan, workspace, name: str, dtype, shape):
 
 
 def attention(q, k, v, frames, grid_h, grid_w, win_h, win_w, budget_hi, budget_lo, softmax_scale=0.0,
-              out_dtype=None, workspace=None, stream=None):
-    """Convenience wrapper: plan, prepare and attend for contiguous [B, H, N, d] bf16 tensors."""
+              out_dtype=None, workspace=None, stream=None, flags=0):
+    """Convenience wrapper: plan, prepare and attend for bf16 [B, H, N, d]
+    tensors that share one set of strides with d contiguous (for example
+    [B, N, H, d] storage viewed as [B, H, N, d], or slices of a fused QKV
+    tensor). The output gets the same strides."""
     import torch
     B, H, N, d = q.shape
+    st = tuple(q.stride())
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    if tuple(k.stride()) != st or tuple(v.stride()) != st or st[3] != 1:
+        raise ValueError("q, k and v must share their strides, with the last dimension contiguous")
+    if not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
+        raise ValueError("q, k and v must be bfloat16")
     if out_dtype is None:
         out_dtype = torch.bfloat16
     cfg = make_config(B, H, frames, grid_h, grid_w, d, win_h, win_w, budget_hi, budget_lo, softmax_scale,
-                      out_dtype=DA2_OUT_FP32 if out_dtype == torch.float32 else DA2_OUT_BF16)
+                      strides=st[:3], out_dtype=DA2_OUT_FP32 if out_dtype == torch.float32 else DA2_OUT_BF16,
+                      flags=flags)
     plan = da2_plan(cfg)
     ws = plan.workspace(q.device) if workspace is None else workspace
-    out = torch.empty(B, H, N, d, dtype=out_dtype, device=q.device)
+    out = torch.empty_strided((B, H, N, d), st, dtype=out_dtype, device=q.device)
     da2_prepare(plan, q, k, v, ws, stream)
     da2_attention(plan, ws, out, stream)
     return out

@@ -207,3 +207,25 @@ def test_graph_capture_replays_match_eager(da2):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, want[i]), f"replay {rep} differs from the eager result"
+
+
+def test_strided_inputs_match_contiguous(da2):
+    # q, k, v as [B, N, H, d] storage viewed as [B, H, N, d], and as slices
+    # of one fused [B, N, 3, H, d] tensor: the same values give the same
+    # output, bit for bit, as the contiguous layout (batch 2, packed and not)
+    w = dataclasses.replace(S.SMALL, name="strided", batch=2)
+    q, k, v = (t.cuda() for t in S.make_qkv(w))
+    args = (w.frames, w.grid_h, w.grid_w, w.win_h, w.win_w, w.budget_hi, w.budget_lo)
+    for flags in (0, da2.DA2_FLAG_PACK_EDGES):
+        say(f"contiguous, flags={flags}")
+        ref = da2.attention(q, k, v, *args, out_dtype=torch.float32, flags=flags)
+        bnhd = [t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v)]
+        fused = torch.stack([t.transpose(1, 2) for t in (q, k, v)], dim=2).contiguous()   # [B, N, 3, H, d]
+        views = [fused[:, :, i].transpose(1, 2) for i in range(3)]
+        for name, (qq, kk, vv) in (("bnhd", bnhd), ("fused-qkv", views)):
+            assert not qq.is_contiguous() and torch.equal(qq, q)
+            say(f"{name} strides {tuple(qq.stride())}, flags={flags}")
+            out = da2.attention(qq, kk, vv, *args, out_dtype=torch.float32, flags=flags)
+            assert out.stride() == qq.stride()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), f"{name}: output differs from the contiguous layout"
