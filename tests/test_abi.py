@@ -149,3 +149,19 @@ def test_last_hip_error_is_clear_before_any_failure():
     assert da2._lib.da2_last_hip_error(ctypes.byref(name)) == 0
     assert name.value.decode() == "hipSuccess"
     assert da2._lib.da2_last_hip_error(None) == 0
+
+
+def test_wrapper_rejects_mismatched_tensors_before_any_call():
+    import torch
+    q = torch.zeros(1, 2, 64, 32, dtype=torch.bfloat16)
+    args = (1, 8, 8, 4, 4, 0.25, 0.25)
+    kt = torch.zeros(1, 64, 2, 32, dtype=torch.bfloat16).transpose(1, 2)     # other strides
+    with pytest.raises(ValueError, match="strides"):
+        da2.attention(q, kt, q, *args)
+    with pytest.raises(ValueError, match="bfloat16"):
+        da2.attention(q.float(), q.float(), q.float(), *args)
+    with pytest.raises(ValueError, match="shape"):
+        da2.attention(q, q[:, :1], q, *args)
+    dt = torch.zeros(1, 2, 32, 64, dtype=torch.bfloat16).transpose(2, 3)     # d not contiguous
+    with pytest.raises(ValueError, match="contiguous"):
+        da2.attention(dt, dt, dt, *args)
