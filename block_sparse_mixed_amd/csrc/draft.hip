@@ -204,22 +204,42 @@ struct SortState {
 // up holding the first of the pair (e, e ^ jj) when it is the lower element
 // of an ascending pair or the upper element of a descending one.
 // D: the lane distance jj / R when it is known at compile time (0 otherwise)
+// In-lane compare-exchange at a compile-time distance J < R, so that every
+// register index is a constant (a run-time distance would index the arrays
+// dynamically and move them to scratch memory).
+template <int R, int J>
+__device__ __forceinline__ void inlane_step(SortState<R>& st, int base, int k) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (r & J) continue;
+        const int r2 = r | J;
+        const bool fwd = ((base + r) & k) == 0;
+        const bool swap = fwd != before(st.v[r], st.ix[r], st.v[r2], st.ix[r2]);
+        const double a = st.v[r], b = st.v[r2];
+        const int ia = st.ix[r], ib = st.ix[r2];
+        st.v[r] = swap ? b : a;
+        st.v[r2] = swap ? a : b;
+        st.ix[r] = swap ? ib : ia;
+        st.ix[r2] = swap ? ia : ib;
+    }
+}
+
+// run-time distance jj < R -> the matching compile-time step
+template <int R, int J = 1>
+__device__ __forceinline__ void inlane_dispatch(SortState<R>& st, int base, int k, int jj) {
+    if constexpr (J < R) {
+        if (jj == J) {
+            inlane_step<R, J>(st, base, k);
+            return;
+        }
+        inlane_dispatch<R, 2 * J>(st, base, k, jj);
+    }
+}
+
 template <int R, int D = 0>
 __device__ __forceinline__ void bitonic_step(SortState<R>& st, double* val, int32_t* idx, int base, int k, int jj) {
     if (jj < R) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (r & jj) continue;
-            const int r2 = r | jj;
-            const bool fwd = ((base + r) & k) == 0;
-            const bool swap = fwd != before(st.v[r], st.ix[r], st.v[r2], st.ix[r2]);
-            const double a = st.v[r], b = st.v[r2];
-            const int ia = st.ix[r], ib = st.ix[r2];
-            st.v[r] = swap ? b : a;
-            st.v[r2] = swap ? a : b;
-            st.ix[r] = swap ? ib : ia;
-            st.ix[r2] = swap ? ia : ib;
-        }
+        inlane_dispatch<R>(st, base, k, jj);
         return;
     }
     double pv[R];
