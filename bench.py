@@ -22,8 +22,10 @@ kernel's sources (attn.hip, common.hpp) they were taken on; when the source has 
 field is null.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan480p]
-       [--no-cpu-baseline]
+       [--no-cpu-baseline] [--cpu-heads H] [--cpu-workers P]
        python bench.py --copy-calibration   (counter calibration run only)
+       python bench.py --all-configs        (every workload at its own budgets, one JSON
+                                             line each, with the error against dense fp32)
        python bench.py --sweep              (budget sweep on the Wan-480p shape, one
                                              JSON line per point, with the error
                                              against dense fp32 attention)
@@ -57,7 +59,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan480p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-blocks", type=int, default=12)
+    ap.add_argument("--cpu-heads", type=int, default=1,
+                    help="heads of the workload the CPU oracle baseline runs in full (preparation and every query block)")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle processes (0: the CPUs this process may use, at most 16)")
+    ap.add_argument("--error-rows", type=int, default=2048,
+                    help="query rows per head sampled for the error against dense fp32 attention")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="one JSON line per workload (tiny, small, wan480p, hunyuan720p): times and error vs dense fp32")
     ap.add_argument("--sweep", action="store_true",
                     help="budget sweep on the Wan-480p shape: time and error vs dense fp32 per point")
     ap.add_argument("--sweep-rows", type=int, default=2048,
@@ -130,37 +139,107 @@ def flops(w, nb, n_hi, n_lo):
     return dense, f_hi, f_lo
 
 
-def cpu_baseline(w, q, k, v, n_blocks_sample):
-    """The oracle as it stands, single-threaded BLAS, on a bounded sample:
-    one head's full preparation (geometry, pooling, draft map, ranking,
-    quantization) plus attention for a few query blocks; extrapolated to the
-    whole workload in the metric's unit."""
-    import numpy as np
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_worker_init():
     from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+    import oracle.pipeline  # noqa: F401  (imported before the timed region)
+
+
+_ORACLE_HEADS = {}
+
+
+def _oracle_ready(_):
+    time.sleep(0.1)         # long enough that every worker takes one of these
+    return os.getpid()
+
+
+def _oracle_chunk(task):
+    """One worker's share of the oracle baseline: the whole preparation of
+    the head (once per worker and head), then attention for its query blocks.
+    Returns (head, preparation seconds or 0 when cached, attention seconds,
+    worker pid)."""
+    import numpy as np
 
     from oracle import pipeline as P
-    with threadpool_limits(limits=1):
-        f = lambda t: t[0, 0].float().numpy().astype(np.float64)
+    cfg, head, bits, blocks = task
+    prep = 0.0
+    if head not in _ORACLE_HEADS:
         t0 = time.perf_counter()
-        st = P.prepare_head(w, f(q), f(k), f(v))
-        t_prep = time.perf_counter() - t0
-        nb = st.geo.n_blocks
-        blocks = [int(b) for b in np.linspace(0, nb - 1, n_blocks_sample).round()]
+        f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        import types
+        _ORACLE_HEADS[head] = P.prepare_head(types.SimpleNamespace(**cfg), *(f(b) for b in bits))
+        prep = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    P.attention_raster(_ORACLE_HEADS[head], blocks=blocks)
+    return head, prep, time.perf_counter() - t0, os.getpid()
+
+
+def cpu_baseline(w, q, k, v, heads, workers):
+    """The oracle as it stands, timed on the host CPUs: a pool of `workers`
+    spawned processes with one BLAS thread each runs the whole path
+    (geometry, pooling, draft map, ranking, quantization, attention) for
+    every query block of the first `heads` heads. Each worker prepares the
+    heads it serves itself (in parallel with the others), then attends its
+    share of the query blocks. The value is the dense-equivalent work of
+    those heads over the measured wall time (heads carry equal work, so it
+    is the rate of the whole workload)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    import numpy as np
+
+    from oracle.geometry import Geometry
+    cfg = {k2: getattr(w, k2) for k2 in ("frames", "grid_h", "grid_w", "head_dim", "win_h", "win_w",
+                                          "budget_hi", "budget_lo", "pack_edges")}
+    nb = Geometry(w.frames, w.grid_h, w.grid_w, w.win_h, w.win_w, pack_edges=w.pack_edges).n_blocks
+    bits = lambda t, h: t[0, h].contiguous().view(torch_int16()).numpy().view(np.uint16)
+    per_head = max(1, workers // heads)
+    tasks = []
+    for h in range(heads):
+        b3 = (bits(q, h), bits(k, h), bits(v, h))
+        for c in range(per_head):
+            tasks.append((cfg, h, b3, list(range(c, nb, per_head))))
+    ctx = mp.get_context("spawn")
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=ctx, initializer=_oracle_worker_init) as ex:
+        list(ex.map(_oracle_ready, range(2 * workers)))             # every worker up, imports done
         t0 = time.perf_counter()
-        P.attention_raster(st, blocks=blocks)
-        t_att = (time.perf_counter() - t0) / len(blocks)
-    per_head = t_prep + t_att * nb
-    total = per_head * w.batch * w.heads
-    dense, _, _ = flops(w, nb, st.n_hi, st.n_lo)
+        res = list(ex.map(_oracle_chunk, tasks))
+        wall = time.perf_counter() - t0
+    preps = [r[1] for r in res if r[1] > 0]
+    atts = [r[2] for r in res]
+    dense, _, _ = flops(w, nb, 0, 0)
+    dense_heads = dense * heads / (w.batch * w.heads)
     return {
-        "value": dense / total / 1e12,
+        "value": dense_heads / wall / 1e12,
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": len({r[3] for r in res}),
         "kind": "oracle",
-        "sample": (f"head 0 of {w.batch * w.heads}: full preparation ({t_prep:.1f} s) + attention for "
-                   f"{len(blocks)} of {nb} query blocks ({t_att:.2f} s each); extrapolated to all blocks and "
-                   f"heads: {total:.0f} s per step"),
+        "sample": (f"{heads} of {w.batch * w.heads} heads in full (preparation + all {nb} query blocks), "
+                   f"{workers} spawned processes with 1 BLAS thread each; wall {wall:.1f} s"),
+        "cpu_model": _cpu_model(),
+        "wall_s": wall,
+        # per stage: one whole-head preparation (each worker prepares the heads
+        # it serves, all at once), and attention in core-seconds per query block
+        "stage_s": {"prepare_per_head": sum(preps) / max(1, len(preps)),
+                    "attention_core_s_per_block": sum(atts) / (heads * nb)},
+        "extrapolated_step_s": wall * (w.batch * w.heads) / heads,
     }
+
+
+def torch_int16():
+    import torch
+    return torch.int16
 
 
 def dense_error(q, k, v, out, tau, rows_per_head, seed=0):
@@ -339,6 +418,14 @@ def sweep(args):
         del ws, out, plan
 
 
+def default_workers():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def time_layout(w, qd, kd, vd, pack, steps, warmup):
     """Plan the workload in one block layout and time `steps` whole steps
     (prepare + attention) on the current stream with HIP events, after
@@ -378,7 +465,34 @@ def time_layout(w, qd, kd, vd, pack, steps, warmup):
     prep_ms = [e[0].elapsed_time(e[1]) for e in events]
     attn_ms = [e[1].elapsed_time(e[2]) for e in events]
     step_ms = [e[0].elapsed_time(e[2]) for e in events]
-    return plan.info, prep_ms, attn_ms, step_ms, wall
+    return plan.info, prep_ms, attn_ms, step_ms, wall, out
+
+
+def all_configs(args):
+    """Every workload at its own budgets: step, preparation and attention
+    times, throughput, roofline fraction and error vs dense fp32 (bf16
+    output, the production path)."""
+    import torch
+
+    import synthetic as S
+    for name in ("tiny", "small", "wan480p", "hunyuan720p"):
+        w = S.WORKLOADS[name]
+        q, k, v = (t.to("cuda:0") for t in S.make_qkv(w))
+        info, prep_ms, attn_ms, step_ms, wall, out = time_layout(w, q, k, v, False, args.steps, args.warmup)
+        dense, f_hi, f_lo = flops(w, info.n_blocks, info.n_hi, info.n_lo)
+        t_star = f_hi / P_FP8 + f_lo / P_FP4
+        att_s = sum(attn_ms) / len(attn_ms) / 1e3
+        step_s = sum(step_ms) / len(step_ms) / 1e3
+        err = dense_error(q, k, v, out, info.tau, args.error_rows)
+        print(json.dumps({"workload": name, "n_blocks": info.n_blocks, "n_hi": info.n_hi, "n_lo": info.n_lo,
+                          "attention_ms": att_s * 1e3, "attention_ms_min": min(attn_ms),
+                          "prepare_ms": sum(prep_ms) / len(prep_ms), "step_ms_events": step_s * 1e3,
+                          "dense_equiv_tflops_step": dense / step_s / 1e12,
+                          "attention_executed_tflops": (f_hi + f_lo) / att_s / 1e12,
+                          "blended_roofline_frac": t_star / att_s,
+                          "error_vs_dense_fp32": err}), flush=True)
+        del q, k, v, out
+        torch.cuda.empty_cache()
 
 
 def main():
@@ -388,6 +502,9 @@ def main():
         return
     if args.sweep:
         sweep(args)
+        return
+    if args.all_configs:
+        all_configs(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -404,13 +521,19 @@ def main():
         w = dataclasses.replace(w, name=w.name + "-packed", pack_edges=True)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, q, k, v, args.cpu_sample_blocks)
+        workers = args.cpu_workers or default_workers()
+        cpu = cpu_baseline(w, q, k, v, min(args.cpu_heads, w.batch * w.heads), workers)
     dev = torch.device("cuda:0")
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
-    info, prep_ms, attn_ms, step_ms, wall = time_layout(w, qd, kd, vd, args.pack_edges, args.steps, args.warmup)
+    info, prep_ms, attn_ms, step_ms, wall, out = time_layout(w, qd, kd, vd, args.pack_edges, args.steps, args.warmup)
+    err = dense_error(qd, kd, vd, out, info.tau, args.error_rows)
+    del out
     alt = None
     if not args.no_alt_layout:
-        a_info, a_prep, a_attn, a_step, _ = time_layout(w, qd, kd, vd, not args.pack_edges, args.steps, args.warmup)
+        a_info, a_prep, a_attn, a_step, _, a_out = time_layout(w, qd, kd, vd, not args.pack_edges, args.steps,
+                                                               args.warmup)
+        a_err = dense_error(qd, kd, vd, a_out, a_info.tau, args.error_rows)
+        del a_out
         a_dense, a_hi, a_lo = flops(w, a_info.n_blocks, a_info.n_hi, a_info.n_lo)
         a_attn_s = sum(a_attn) / len(a_attn) / 1e3
         a_step_s = sum(a_step) / len(a_step) / 1e3
@@ -419,7 +542,8 @@ def main():
                "attention_ms": a_attn_s * 1e3, "prepare_ms": sum(a_prep) / len(a_prep),
                "step_ms_events": a_step_s * 1e3,
                "dense_equiv_tflops_step_events": a_dense / a_step_s / 1e12,
-               "roofline_frac": (a_hi / P_FP8 + a_lo / P_FP4) / a_attn_s}
+               "roofline_frac": (a_hi / P_FP8 + a_lo / P_FP4) / a_attn_s,
+               "error_vs_dense_fp32": a_err}
     ms_per_step = wall * 1e3 / args.steps
     dense, f_hi, f_lo = flops(w, info.n_blocks, info.n_hi, info.n_lo)
     t_star = f_hi / P_FP8 + f_lo / P_FP4
@@ -449,6 +573,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": blended_peak / 1e12, "unit": "TFLOP/s",
                      "frac": achieved / blended_peak, "traffic": recorded_traffic(w.name)},
         "cpu_baseline": cpu,
+        "error_vs_dense_fp32": err,
         "attention_ms": sum(attn_ms) / len(attn_ms),
         "attention_ms_min": min(attn_ms),
         "prepare_ms": sum(prep_ms) / len(prep_ms),

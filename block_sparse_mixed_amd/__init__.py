@@ -213,12 +213,19 @@ def attention(q, k, v, frames, grid_h, grid_w, win_h, win_w, budget_hi, budget_l
     st = tuple(q.stride())
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k and v must have the same shape")
+    if N != frames * grid_h * grid_w:
+        raise ValueError(f"q has {N} tokens, but a {frames} x {grid_h} x {grid_w} latent grid has "
+                         f"{frames * grid_h * grid_w}")
     if tuple(k.stride()) != st or tuple(v.stride()) != st or st[3] != 1:
         raise ValueError("q, k and v must share their strides, with the last dimension contiguous")
     if not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
         raise ValueError("q, k and v must be bfloat16")
     if out_dtype is None:
         out_dtype = torch.bfloat16
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+    if q.device.type != "cuda" or k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on one GPU device")
     cfg = make_config(B, H, frames, grid_h, grid_w, d, win_h, win_w, budget_hi, budget_lo, softmax_scale,
                       strides=st[:3], out_dtype=DA2_OUT_FP32 if out_dtype == torch.float32 else DA2_OUT_BF16,
                       flags=flags)

@@ -297,8 +297,8 @@ struct WaveState {
     v16f lsum;             // the query's row sum (all sixteen elements equal)
     float m;               // running integer max (log2 units)
     float mref;            // acc and lsum hold values relative to 2^mref
-    float c_lo;            // tau * log2(e)
-    float c_hi_q;          // tau * log2(e) * 2^e_q8
+    float c_lo;            // tau * log2(e), at least FLT_MIN
+    int e_q;               // fp8 block exponent of the query block
 };
 
 // A 32x32x64 MFMA operand in E2M1 occupies four registers; the builtin takes
@@ -521,7 +521,12 @@ constexpr float kMaxLead = 64.0f;
 template <int PH, class Fetch>
 __device__ __forceinline__ void softmax(WaveState& st, const v16f (&s)[4], int e_k, v8i (&pop)[2], int (&psc)[2],
                                         Fetch&& fetch) {
-    const float cs = PH == kHi ? ldexpf(st.c_hi_q, e_k) : st.c_lo;
+    // fp8 tiles: the codes' product carries 2^(e_q + e_k), applied in one
+    // step (no intermediate underflow) and kept at least FLT_MIN, so that a
+    // padded key's -inf score stays -inf (0 * -inf would be NaN) when the
+    // two blocks' magnitudes are so small that the factor underflows; the
+    // real scores are then below 2^-100 in either case
+    const float cs = PH == kHi ? fmaxf(ldexpf(st.c_lo, st.e_q + e_k), __FLT_MIN__) : st.c_lo;
     float gmax[2];                                       // per PV MFMA n: the lane's 32 raw scores
     block_max(s, gmax);
     const float mnew = fmaxf(st.m, ceilf(cross2max(vmax(gmax[0], gmax[1])) * cs));
@@ -789,12 +794,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) st.acc[cb][e] = 0.f;
     }
-    st.c_lo = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, (float)g.tau * kLog2E)));
-    {
-        // uniform: kept in a scalar register
-        const float c = ldexpf(st.c_lo, __builtin_amdgcn_readfirstlane((int)ws[a.L.e8 + qtile]) - 127);
-        st.c_hi_q = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c)));
-    }
+    // uniform values, kept in scalar registers
+    st.c_lo = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, fmaxf((float)g.tau * kLog2E, __FLT_MIN__))));
+    st.e_q = __builtin_amdgcn_readfirstlane((int)ws[a.L.e8 + qtile]) - 127;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 

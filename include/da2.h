@@ -23,6 +23,13 @@
  *    element strides (stride_b, stride_h, stride_n), head_dim contiguous.
  *    Tokens are in raster order (frame, row, column) of a frames x grid_h x
  *    grid_w latent grid. q, k, v are bf16; out is bf16 or fp32.
+ *  - Rows are read and written as 16-byte vectors: the q, k, v and out
+ *    pointers must be 16-byte aligned and the three strides multiples of 8
+ *    elements; otherwise da2_prepare / da2_attention return
+ *    DA2_ERR_UNSUPPORTED before enqueuing anything.
+ *  - Every call that takes a workspace also takes its size in bytes
+ *    (workspace_bytes): a buffer smaller than the plan's workspace_bytes, or
+ *    not 256-byte aligned, is DA2_ERR_WORKSPACE.
  *  - Argument errors are reported synchronously, before anything is enqueued.
  *    Kernel faults surface at the caller's next synchronisation, as usual in
  *    HIP. No C++ exception crosses this interface.
@@ -78,9 +85,9 @@ typedef struct da2_config {
     int32_t frames;
     int32_t grid_h;           /* latent rows per frame */
     int32_t grid_w;           /* latent columns per frame */
-    int32_t head_dim;         /* 32, 64, 96 or 128 */
+    int32_t head_dim;         /* 32, 64, 96 or 128 (other positive values: DA2_ERR_UNSUPPORTED) */
     int32_t win_h;            /* pooling window = one block: win_h x win_w tokens */
-    int32_t win_w;            /* win_h * win_w <= 128 */
+    int32_t win_w;            /* win_h * win_w <= 128 (larger: DA2_ERR_UNSUPPORTED) */
     double budget_hi;         /* fraction of key blocks per query block in fp8 */
     double budget_lo;         /* fraction in MXFP4 (clamped to 1 - budget_hi) */
     double softmax_scale;     /* tau; 0 selects 1/sqrt(head_dim) */
@@ -138,6 +145,12 @@ typedef struct da2_plan_info_s {
 } da2_plan_info_t;
 
 /* Validate cfg and build a plan. Host only: touches no GPU state.
+ * Errors: DA2_ERR_INVALID_ARG for a NULL argument, a non-positive size,
+ * negative strides (or stride_n < head_dim, or a zero stride_b / stride_h
+ * when any stride is given), budgets outside [0, 1] or not finite, a
+ * negative or non-finite softmax_scale, an unknown out_dtype or flag bit,
+ * or n_ret = 0; DA2_ERR_UNSUPPORTED for a head_dim or window outside the
+ * domains above, more than DA2_MAX_BLOCKS blocks, or batch * heads > 65535.
  * Geometry [DraftAttention (arXiv 2505.14708), abstract; news article on it,
  * method steps 1 and 4]: each frame is cut into win_h x win_w windows, padded
  * up to whole windows; a window is one block (with DA2_FLAG_PACK_EDGES: the

@@ -165,3 +165,34 @@ def test_wrapper_rejects_mismatched_tensors_before_any_call():
     dt = torch.zeros(1, 2, 32, 64, dtype=torch.bfloat16).transpose(2, 3)     # d not contiguous
     with pytest.raises(ValueError, match="contiguous"):
         da2.attention(dt, dt, dt, *args)
+    # the token count must be the latent grid's: fewer rows would be read and
+    # written past the tensors' ends, more would be left unwritten
+    for grid in ((1, 8, 7), (2, 8, 8)):
+        with pytest.raises(ValueError, match="latent grid"):
+            da2.attention(q, q, q, *grid, *args[3:])
+    # the tensors must be on a GPU (these are on the CPU), and the output
+    # dtype one the library writes
+    with pytest.raises(ValueError, match="GPU"):
+        da2.attention(q, q, q, *args)
+    with pytest.raises(ValueError, match="out_dtype"):
+        da2.attention(q, q, q, *args, out_dtype=torch.float16)
+
+
+def test_enqueue_calls_reject_unaligned_pointers_and_strides():
+    # q, k, v and out are read and written in 16-byte vectors: their pointers
+    # must be 16-byte aligned and the strides multiples of 8 elements, else
+    # DA2_ERR_UNSUPPORTED, reported before anything is enqueued
+    lib = da2._lib
+    fake = 1 << 20
+    big = 1 << 40
+    p = da2.da2_plan(_cfg())
+    for off in (2, 8):
+        assert lib.da2_prepare(p.handle, fake + off, fake, fake, fake, big, None) == da2.DA2_ERR_UNSUPPORTED
+        assert lib.da2_prepare(p.handle, fake, fake, fake + off, fake, big, None) == da2.DA2_ERR_UNSUPPORTED
+        assert lib.da2_attention(p.handle, fake, big, fake + off, None) == da2.DA2_ERR_UNSUPPORTED
+    n = 32760
+    for strides in ((12 * n * 132, n * 132, 132), (12 * n * 128 + 4, n * 128, 128), (12 * n * 128, n * 128 + 2, 128),
+                    (12 * n * 129, n * 129, 129)):
+        p = da2.da2_plan(_cfg(strides=strides))
+        assert lib.da2_prepare(p.handle, fake, fake, fake, fake, big, None) == da2.DA2_ERR_UNSUPPORTED
+        assert lib.da2_attention(p.handle, fake, big, fake, None) == da2.DA2_ERR_UNSUPPORTED

@@ -16,6 +16,7 @@ import synthetic as S
 from oracle import draft as D
 from oracle import pipeline as P
 
+import oracle_pool as OP
 from gpu_cases import OUT_TOL, GpuRun, block_rows, check_prepare, compare_outputs, np64, say
 
 pytestmark = pytest.mark.gpu
@@ -28,13 +29,14 @@ def da2():
     return m
 
 
-def _full_parity(da2, w, heads=None, att_blocks=None):
-    run = GpuRun(da2, w)
+def _full_parity(da2, w, heads=None, att_blocks=None, run=None, states=None):
+    run = GpuRun(da2, w) if run is None else run
     heads = range(run.bh) if heads is None else heads
-    states = {bh: run.oracle_head(bh) for bh in heads}
-    for bh, st in states.items():
-        say(f"check prepare {w.name} bh={bh}")
-        check_prepare(run, bh, st)
+    if states is None:
+        states = {bh: run.oracle_head(bh) for bh in heads}
+        for bh, st in states.items():
+            say(f"check prepare {w.name} bh={bh}")
+            check_prepare(run, bh, st)
     # attention with the oracle's own labels injected
     labels = np.zeros((run.bh, run.nb, run.nb), dtype=np.int8)
     full_labels = {bh: st.labels for bh, st in states.items()}
@@ -90,17 +92,73 @@ def test_bf16_output_is_rne_of_fp32(da2):
     assert torch.equal(o16, o32.to(torch.bfloat16))
 
 
-def test_wan_shape_sampled(da2):
-    # full-size launch; codes/labels for two heads, outputs on sampled query
-    # blocks including the partial edge windows (3, 15) and a frame boundary
-    _full_parity(da2, S.WAN480, heads=[0, 7], att_blocks=[0, 3, 15, 16, 170, 335])
+def _bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 CPU tensor -> its uint16 bit patterns."""
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
-def test_hunyuan_shape_sampled(da2):
-    # the largest shape: 24 heads x 118800 tokens, 990 blocks (rows of windows
-    # partial in y); codes/labels for the first and last head, outputs on
-    # sampled query blocks including a partial window (29) and the last block
-    _full_parity(da2, S.HUNYUAN720, heads=[0, 23], att_blocks=[0, 29, 500, 989])
+def _headline(da2, w, heads, blocks, inject_blocks):
+    """The path the benchmark times, end to end: the GPU's own labels and its
+    rank-ordered lists (no injection), then
+      * codes, scales, pools, scores, labels and lists of `heads` against the oracle;
+      * bf16 output of the same workspace = RNE of the fp32 output, every head;
+      * fp32 output of `blocks` (None: all) of `heads` against the oracle,
+        on every query block whose label row equals the oracle's (the others
+        differ only inside the exemption band, checked above);
+    and finally the oracle's labels injected, outputs on `inject_blocks`."""
+    run = GpuRun(da2, w)
+    out32 = run.attend(out_fp32=True)
+    cfg_bf = da2.make_config(w.batch, w.heads, w.frames, w.grid_h, w.grid_w, w.head_dim, w.win_h, w.win_w,
+                             w.budget_hi, w.budget_lo, out_dtype=da2.DA2_OUT_BF16)
+    plan_bf = da2.da2_plan(cfg_bf)
+    out16 = torch.empty(w.batch, w.heads, w.tokens, w.head_dim, dtype=torch.bfloat16, device="cuda")
+    say(f"da2_attention bf16 {w.name}")
+    da2.da2_attention(plan_bf, run.ws, out16)
+    torch.cuda.synchronize()
+    assert torch.equal(out16, out32.to(torch.bfloat16)), "bf16 output is not RNE of the fp32 output"
+    lab = run.sec("labels", torch.int8, (run.bh, run.nb, run.nb))
+    o = np64(out32.reshape(run.bh, w.tokens, w.head_dim))
+    states = {}
+    for bh in heads:
+        st = run.oracle_head(bh)
+        states[bh] = st
+        say(f"check prepare {w.name} bh={bh}")
+        check_prepare(run, bh, st)
+        want_blocks = range(run.nb) if blocks is None else blocks
+        same = (lab[bh] == st.labels).all(axis=1)
+        use = [int(i) for i in want_blocks if same[i]]
+        say(f"   {len(use)} of {len(want_blocks)} query blocks have the oracle's label row")
+        assert len(use) >= 0.95 * len(want_blocks)
+        b, h = divmod(bh, w.heads)
+        rows, want = OP.attention_rows(w, _bits(run.qc[b, h]), _bits(run.kc[b, h]), _bits(run.vc[b, h]), use)
+        say(f"   oracle rows {len(rows)} (pool of {OP.pool_size()})")
+        assert np.array_equal(rows, np.sort(block_rows(st, use)))
+        full = np.full((w.tokens, w.head_dim), np.nan)
+        full[rows] = want
+        worst, _ = compare_outputs(o[bh], full, rows)
+        assert worst <= OUT_TOL, f"{w.name} bh={bh}: max |gpu - oracle| = {worst}"
+    _full_parity(da2, w, heads=heads, att_blocks=inject_blocks, run=run, states=states)
+    return run, states
+
+
+@pytest.mark.timeout(900)
+def test_wan_shape_end_to_end_all_blocks(da2):
+    # every query block of two heads (incl. the partial edge windows and
+    # frame boundaries), GPU labels and lists; then the injected-label path
+    # on sampled blocks
+    _headline(da2, S.WAN480, heads=[0, 7], blocks=None, inject_blocks=[0, 3, 15, 16, 170, 335])
+
+
+@pytest.mark.timeout(900)
+def test_hunyuan_shape_end_to_end_sampled(da2):
+    # the largest shape: 24 heads x 118800 tokens, 990 blocks (the last row
+    # of windows is 5 rows high); the first and last head, a seeded sample of
+    # query blocks with at least 4096 real rows per head, incl. a partial
+    # window (29) and the last block
+    rng = np.random.default_rng(1)
+    blocks = sorted(set(rng.choice(990, 36, replace=False).tolist()) | {0, 29, 500, 989})
+    run, states = _headline(da2, S.HUNYUAN720, heads=[0, 23], blocks=blocks, inject_blocks=[0, 29, 500, 989])
+    assert len(block_rows(states[0], blocks)) >= 4096
 
 
 @pytest.mark.parametrize("hi,lo", [(0.05, 0.0), (0.05, 0.4), (0.1, 0.2), (0.25, 0.2), (0.25, 0.4), (1.0, 0.0),
@@ -120,9 +178,68 @@ def test_edge_shapes(da2):
         dataclasses.replace(S.TINY, name="d64w128", frames=2, grid_h=16, grid_w=32, win_h=8, win_w=16,
                             head_dim=64, budget_hi=0.25, budget_lo=0.5),
         dataclasses.replace(S.TINY, name="batch2", batch=2, heads=3, frames=2, grid_h=8, grid_w=8),
+        # the other head sizes the plan accepts: 32 and 96 channels (one and
+        # three MX groups of 32, the rest of the 128-channel tile zero)
+        dataclasses.replace(S.TINY, name="d32", frames=2, grid_h=16, grid_w=32, win_h=8, win_w=16,
+                            head_dim=32, budget_hi=0.25, budget_lo=0.25),
+        dataclasses.replace(S.TINY, name="d96-ragged", frames=3, grid_h=13, grid_w=21, win_h=8, win_w=16,
+                            head_dim=96, budget_hi=0.2, budget_lo=0.4),
+        # windows of 64 and of 15 (odd) tokens: blocks of any size up to 128
+        dataclasses.replace(S.TINY, name="win8x8", frames=2, grid_h=20, grid_w=20, win_h=8, win_w=8,
+                            head_dim=128, budget_hi=0.15, budget_lo=0.35),
+        dataclasses.replace(S.TINY, name="win3x5", frames=2, grid_h=10, grid_w=11, win_h=3, win_w=5,
+                            head_dim=64, budget_hi=0.2, budget_lo=0.3),
     ]
     for w in cases:
         _full_parity(da2, w)
+
+
+def test_set_labels_counts_rows_with_wrong_counts(da2):
+    # the test hook rejects label rows whose hi/lo counts differ from the
+    # plan's: status[0] is the number of such rows (reset on every call)
+    w = S.TINY
+    run = GpuRun(da2, w)
+    st = run.oracle_head(0)
+    bad = st.labels.copy()
+    skip = np.flatnonzero(bad[3] == D.SKIP)[0]
+    bad[3, skip] = D.HI                                  # one hi too many
+    lo = np.flatnonzero(bad[5] == D.LO)[0]
+    bad[5, lo] = D.SKIP                                  # one lo too few
+    bad[9] = D.SKIP                                      # nothing retained
+    assert run.set_labels(bad[None]) == 3
+    assert run.set_labels(st.labels[None]) == 0
+    out = np64(run.attend()[0, 0])
+    worst, _ = compare_outputs(out, P.attention_raster(st), np.arange(w.tokens))
+    assert worst <= OUT_TOL
+
+
+def test_zero_and_tiny_magnitude_blocks(da2):
+    # windows of Q and K that are all zero, or scaled by 2^-70 so that the
+    # fp8 score factor 2^(e_q + e_k) underflows fp32, next to ordinary ones;
+    # partial windows give padded key slots (which must stay -inf). Ties in
+    # the draft scores of the zero query block put the first key blocks,
+    # including the tiny partial window 1, into its fp8 list.
+    w = dataclasses.replace(S.TINY, name="zero-tiny", frames=3, grid_h=13, grid_w=21, win_h=8, win_w=16,
+                            head_dim=128, budget_hi=0.2, budget_lo=0.4)
+    q, k, v = S.make_qkv(w)
+    grid = lambda t: t.view(w.batch, w.heads, w.frames, w.grid_h, w.grid_w, w.head_dim)
+    tiny = 2.0 ** -70
+    grid(q)[:, :, 0, 0:8, 0:16] = 0                      # block 0: zero queries
+    grid(k)[:, :, 1, 8:13, 16:21] = 0                    # block 7: zero keys (partial window)
+    grid(q)[:, :, 2, 0:8, 16:21] *= tiny                 # block 9: tiny queries (partial window)
+    grid(k)[:, :, 0, 0:8, 16:21] *= tiny                 # block 1: tiny keys (partial window)
+    grid(k)[:, :, 2, 8:13, 0:16] *= tiny                 # block 10: tiny keys
+    run = GpuRun(da2, w, qkv=(q, k, v))
+    st = run.oracle_head(0)
+    assert st.ops["q8_exp"][0] == -127 and st.ops["q8_exp"][9] + st.ops["k8_exp"][1] < -140
+    assert st.labels[0, 1] == D.HI and st.labels[9, 1] != D.SKIP
+    _full_parity(da2, w)
+    out = run.attend()
+    assert torch.isfinite(out).all()
+    lab = run.sec("labels", torch.int8, (1, run.nb, run.nb))[0]
+    same = np.flatnonzero((lab == st.labels).all(axis=1))
+    worst, _ = compare_outputs(np64(out[0, 0]), P.attention_raster(st, blocks=same), block_rows(st, same))
+    assert worst <= OUT_TOL
 
 
 @pytest.mark.parametrize("grid", [66, 94])
