@@ -62,7 +62,8 @@ class PlanInfo(ctypes.Structure):
 
 
 EXPORTS = ("da2_plan", "da2_plan_destroy", "da2_plan_info", "da2_prepare", "da2_attention",
-           "da2_set_labels", "da2_status_string", "da2_last_hip_error")
+           "da2_set_labels", "da2_forward_scratch", "da2_status_string", "da2_last_hip_error")
+SCRATCH_BYTES = 256 << 20      # DA2_SCRATCH_BYTES
 
 
 def _load():
@@ -82,6 +83,8 @@ def _load():
     lib.da2_attention.restype = ctypes.c_int
     lib.da2_set_labels.argtypes = [P, P, ctypes.c_size_t, P, P]
     lib.da2_set_labels.restype = ctypes.c_int
+    lib.da2_forward_scratch.argtypes = [P, P, P, P, P, P]
+    lib.da2_forward_scratch.restype = ctypes.c_int
     lib.da2_status_string.argtypes = [ctypes.c_int]
     lib.da2_status_string.restype = ctypes.c_char_p
     lib.da2_last_hip_error.argtypes = [ctypes.POINTER(ctypes.c_char_p)]
@@ -189,6 +192,12 @@ def da2_set_labels(plan: Plan, workspace, labels, stream=None):
     nbytes = workspace.numel() if hasattr(workspace, "numel") else int(plan.info.workspace_bytes)
     _check(_lib.da2_set_labels(plan.handle, _ptr(workspace), nbytes, _ptr(labels), _stream(stream)),
            "da2_set_labels")
+
+
+def da2_forward_scratch(plan: Plan, q, k, v, out, stream=None):
+    """da2_prepare + da2_attention on the library's static workspace (no allocation)."""
+    _check(_lib.da2_forward_scratch(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _stream(stream)),
+           "da2_forward_scratch")
 
 
 def workspace_section(plan: Plan, workspace, name: str, dtype, shape):

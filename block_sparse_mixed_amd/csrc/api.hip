@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "da2_internal.hpp"
 
@@ -81,4 +82,67 @@ extern "C" da2_status da2_set_labels(const da2_plan_t* plan, void* workspace, si
 extern "C" int da2_last_hip_error(const char** name) {
     if (name) *name = hipGetErrorName(g_last_hip);
     return static_cast<int>(g_last_hip);
+}
+
+// ---- the entry point that allocates nothing ----
+// Its workspace is this file-scope device array (one copy per GPU, held
+// until the process ends). In host code the name `scratch` is only a
+// stand-in for the symbol, never a device address: host code uses the
+// address hipGetSymbolAddress returns for the device, looked up once per
+// device with that device current and kept in g_scratch.
+namespace {
+
+static __device__ __align__(256) __attribute__((used)) uint8_t scratch[DA2_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];   // device address of `scratch` per device, null until looked up
+
+// The device address of `scratch` on the device that runs `stream`.
+da2_status scratch_address(hipStream_t stream, void** out) {
+    int cur = -1;
+    if (hipError_t e = hipGetDevice(&cur); e != hipSuccess) return hip_fail(e);
+    int dev = cur;
+    if (stream) {
+        hipDevice_t d = 0;
+        if (hipError_t e = hipStreamGetDevice(stream, &d); e != hipSuccess) return hip_fail(e);
+        dev = static_cast<int>(d);
+    }
+    if (dev < 0 || dev >= kMaxDevices) return DA2_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        if (dev != cur)
+            if (hipError_t e = hipSetDevice(dev); e != hipSuccess) return hip_fail(e);
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess && r != hipSuccess) return hip_fail(r);
+        }
+        if (e != hipSuccess) return hip_fail(e);
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return DA2_OK;
+}
+
+}  // namespace
+
+extern "C" da2_status da2_forward_scratch(const da2_plan_t* plan, const void* q, const void* k, const void* v,
+                                          void* out, void* hip_stream) {
+    if (!plan || !q || !k || !v || !out) return DA2_ERR_INVALID_ARG;
+    if (plan->ws.total > DA2_SCRATCH_BYTES) return DA2_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !strides_vectorizable(plan->geo))
+        return DA2_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    void* ws = nullptr;
+    if (da2_status st = scratch_address(s, &ws); st != DA2_OK) return st;
+    // every byte of the workspace that a later kernel reads is written by an
+    // earlier one in this call, so the array needs no clearing between calls
+    if (hipError_t e = da2::launch_prep(plan->geo, plan->ws, q, k, v, ws, s); e != hipSuccess) return hip_fail(e);
+    if (hipError_t e = da2::launch_draft(plan->geo, plan->ws, ws, s); e != hipSuccess) return hip_fail(e);
+    const int out_fp32 = plan->cfg.out_dtype == DA2_OUT_FP32;
+    if (hipError_t e = da2::launch_attention(plan->geo, plan->ws, ws, out, out_fp32, s); e != hipSuccess)
+        return hip_fail(e);
+    return DA2_OK;
 }

@@ -16,9 +16,11 @@
  *
  * Conventions
  *  - Every device buffer (q, k, v, out, workspace, labels) is allocated and
- *    owned by the caller. The library allocates no device memory and keeps no
- *    global mutable state; a plan is an immutable host object, so calls on
- *    different plans (or the same plan from different threads) are safe.
+ *    owned by the caller. The library allocates no device memory; a plan is
+ *    an immutable host object, so calls on different plans (or the same plan
+ *    from different threads) are safe. The one exception is
+ *    da2_forward_scratch, whose workspace is a static device array of the
+ *    library shared by all its calls on a GPU (see there).
  *  - Tensors q, k, v, out are [batch, heads, tokens, head_dim] addressed by
  *    element strides (stride_b, stride_h, stride_n), head_dim contiguous.
  *    Tokens are in raster order (frame, row, column) of a frames x grid_h x
@@ -78,6 +80,8 @@ enum { DA2_SKIP = 0, DA2_LO = 1, DA2_HI = 2 };
 #define DA2_TILE 128
 #define DA2_DPAD 128
 #define DA2_MAX_BLOCKS 4096
+/* Size of the library's own static workspace, used by da2_forward_scratch. */
+#define DA2_SCRATCH_BYTES (256ull << 20)
 
 typedef struct da2_config {
     int32_t batch;
@@ -205,6 +209,22 @@ da2_status da2_attention(const da2_plan_t* plan, const void* workspace, size_t w
  * count is reset first) and its lists are left unspecified. Asynchronous. */
 da2_status da2_set_labels(const da2_plan_t* plan, void* workspace, size_t workspace_bytes,
                           const int8_t* labels_dev, void* hip_stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the work
+ * of da2_prepare followed by da2_attention, with the library's own static
+ * workspace of DA2_SCRATCH_BYTES (256 MiB) per GPU instead of a caller's
+ * buffer. Same arguments, layouts, results and errors as that pair; a plan
+ * whose workspace_bytes exceeds DA2_SCRATCH_BYTES is DA2_ERR_WORKSPACE (for
+ * example Wan-480p-sized calls of up to 7 heads fit, Hunyuan-720p-sized of up
+ * to 2). Allocates nothing: the static array is a device global of the
+ * library's code object, held on each GPU the library runs on until the
+ * process ends; its address is looked up once per device (on the device of
+ * hip_stream). Every call on one GPU uses the same array, which keeps the
+ * last call's contents: calls that may overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller. Asynchronous. */
+da2_status da2_forward_scratch(const da2_plan_t* plan, const void* q, const void* k, const void* v, void* out,
+                               void* hip_stream);
 
 /* Static, never-NULL description of a status code. */
 const char* da2_status_string(da2_status status);

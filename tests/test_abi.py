@@ -196,3 +196,20 @@ def test_enqueue_calls_reject_unaligned_pointers_and_strides():
         p = da2.da2_plan(_cfg(strides=strides))
         assert lib.da2_prepare(p.handle, fake, fake, fake, fake, big, None) == da2.DA2_ERR_UNSUPPORTED
         assert lib.da2_attention(p.handle, fake, big, fake, None) == da2.DA2_ERR_UNSUPPORTED
+
+
+def test_forward_scratch_rejects_calls_beyond_the_static_workspace():
+    # the no-allocation entry point checks its arguments before touching the
+    # GPU: a plan whose workspace exceeds the library's static array (a whole
+    # Wan-480p step, 12 heads: 393 MiB > 256 MiB) is DA2_ERR_WORKSPACE, and
+    # the pointer and stride rules are those of prepare / attention
+    lib = da2._lib
+    fake = 1 << 20
+    big = da2.da2_plan(_cfg())
+    assert big.info.workspace_bytes > da2.SCRATCH_BYTES
+    assert lib.da2_forward_scratch(big.handle, fake, fake, fake, fake, None) == da2.DA2_ERR_WORKSPACE
+    small = da2.da2_plan(_cfg(heads=6))
+    assert small.info.workspace_bytes <= da2.SCRATCH_BYTES
+    assert lib.da2_forward_scratch(small.handle, fake, fake, fake, fake + 4, None) == da2.DA2_ERR_UNSUPPORTED
+    assert lib.da2_forward_scratch(small.handle, fake, None, fake, fake, None) == da2.DA2_ERR_INVALID_ARG
+    assert lib.da2_forward_scratch(None, fake, fake, fake, fake, None) == da2.DA2_ERR_INVALID_ARG
