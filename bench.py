@@ -26,6 +26,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan480p]
        python bench.py --copy-calibration   (counter calibration run only)
        python bench.py --all-configs        (every workload at its own budgets, one JSON
                                              line each, with the error against dense fp32)
+       python bench.py --dit-block          (the DiT attention sublayer: fused custom op,
+                                             unfused layout copies, dense SDPA)
        python bench.py --sweep              (budget sweep on the Wan-480p shape, one
                                              JSON line per point, with the error
                                              against dense fp32 attention)
@@ -67,6 +69,10 @@ def parse():
                     help="query rows per head sampled for the error against dense fp32 attention")
     ap.add_argument("--all-configs", action="store_true",
                     help="one JSON line per workload (tiny, small, wan480p, hunyuan720p): times and error vs dense fp32")
+    ap.add_argument("--dit-block", action="store_true",
+                    help="time the attention sublayer of a DiT block at the workload's shape (QKV projection, "
+                         "attention, output projection; random weights): the fused custom op, the unfused "
+                         "sequence with layout copies, and dense torch SDPA")
     ap.add_argument("--sweep", action="store_true",
                     help="budget sweep on the Wan-480p shape: time and error vs dense fp32 per point")
     ap.add_argument("--sweep-rows", type=int, default=2048,
@@ -495,6 +501,77 @@ def all_configs(args):
         torch.cuda.empty_cache()
 
 
+def dit_block(args):
+    """The attention sublayer of a video DiT block at the workload's shape,
+    hidden size heads x head_dim, random bf16 weights (timing only):
+      fused   x -> QKV projection -> da2::attention_qkv reading the projection
+              output in place -> output projection reading the op's
+              [B, N, H, d] output in place;
+      unfused the same projections and library call with the usual layout
+              changes around the attention: split + permute of the QKV
+              output to contiguous [B, H, N, d], and the output back to
+              [B, N, H*d];
+      dense   the same projections around torch's scaled_dot_product_attention
+              (bf16, dense) on the permuted q, k, v.
+    Prints one JSON line with the per-step milliseconds of each."""
+    import torch
+    import torch.nn.functional as Fn
+
+    import block_sparse_mixed_amd as da2
+    import synthetic as S
+    from block_sparse_mixed_amd import torch_op
+    w = S.WORKLOADS[args.workload]
+    B, H, d, N = w.batch, w.heads, w.head_dim, w.tokens
+    C = H * d
+    torch.manual_seed(0)
+    m = torch_op.DA2SelfAttention(C, H, w.frames, w.grid_h, w.grid_w, win=(w.win_h, w.win_w),
+                                  budget_hi=w.budget_hi, budget_lo=w.budget_lo,
+                                  flags=da2.DA2_FLAG_PACK_EDGES if args.pack_edges else 0, device="cuda")
+    x = torch.randn(B, N, C, device="cuda", dtype=torch.bfloat16)
+    grid = (w.frames, w.grid_h, w.grid_w, w.win_h, w.win_w, w.budget_hi, w.budget_lo)
+
+    def fused():
+        return m(x)
+
+    def split():
+        qkv = m.qkv(x).view(B, N, 3, H, d).permute(2, 0, 3, 1, 4).contiguous()
+        return qkv[0], qkv[1], qkv[2]
+
+    def unfused():
+        q, k, v = split()
+        o = da2.attention(q, k, v, *grid, out_dtype=torch.bfloat16, flags=m.flags)
+        return m.proj(o.transpose(1, 2).reshape(B, N, C))
+
+    def dense():
+        q, k, v = split()
+        o = Fn.scaled_dot_product_attention(q, k, v)
+        return m.proj(o.transpose(1, 2).reshape(B, N, C))
+
+    def projections():
+        return m.proj(m.qkv(x)[..., :C].contiguous())
+
+    res = {"dit_block": {"workload": w.name, "hidden": C, "heads": H, "tokens": N, "batch": B,
+                         "budget_hi": w.budget_hi, "budget_lo": w.budget_lo,
+                         "layout": "packed_edges" if args.pack_edges else "padded_windows"}}
+    with torch.no_grad():
+        for name, fn in (("fused", fused), ("unfused", unfused), ("dense_sdpa", dense),
+                         ("projections_only", projections)):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name + "_ms"] = e0.elapsed_time(e1) / args.steps
+        y_fused, y_unfused = fused(), unfused()
+        torch.cuda.synchronize()
+        res["fused_equals_unfused"] = bool(torch.equal(y_fused, y_unfused))
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -505,6 +582,9 @@ def main():
         return
     if args.all_configs:
         all_configs(args)
+        return
+    if args.dit_block:
+        dit_block(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "

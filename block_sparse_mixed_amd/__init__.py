@@ -43,6 +43,7 @@ class Config(ctypes.Structure):
         ("budget_hi", ctypes.c_double), ("budget_lo", ctypes.c_double), ("softmax_scale", ctypes.c_double),
         ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64),
         ("out_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("out_stride_b", ctypes.c_int64), ("out_stride_h", ctypes.c_int64), ("out_stride_n", ctypes.c_int64),
     ]
 
 
@@ -165,10 +166,11 @@ class Plan:
 
 
 def make_config(batch, heads, frames, grid_h, grid_w, head_dim, win_h, win_w, budget_hi, budget_lo,
-                softmax_scale=0.0, strides=(0, 0, 0), out_dtype=DA2_OUT_FP32, flags=0) -> Config:
+                softmax_scale=0.0, strides=(0, 0, 0), out_dtype=DA2_OUT_FP32, flags=0,
+                out_strides=(0, 0, 0)) -> Config:
     return Config(batch, heads, frames, grid_h, grid_w, head_dim, win_h, win_w, float(budget_hi),
                   float(budget_lo), float(softmax_scale), int(strides[0]), int(strides[1]), int(strides[2]),
-                  int(out_dtype), int(flags))
+                  int(out_dtype), int(flags), int(out_strides[0]), int(out_strides[1]), int(out_strides[2]))
 
 
 def da2_plan(cfg: Config) -> Plan:

@@ -39,6 +39,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool strides_vectorizable(const da2::Geo& g) {
     return g.stride_n % 8 == 0 && g.stride_h % 8 == 0 && g.stride_b % 8 == 0;
 }
+bool out_strides_vectorizable(const da2::Geo& g) {
+    return g.ostride_n % 8 == 0 && g.ostride_h % 8 == 0 && g.ostride_b % 8 == 0;
+}
 
 }  // namespace
 
@@ -60,7 +63,7 @@ extern "C" da2_status da2_attention(const da2_plan_t* plan, const void* workspac
     if (!plan || !out) return DA2_ERR_INVALID_ARG;
     da2_status st = check_ws(plan, workspace, workspace_bytes);
     if (st != DA2_OK) return st;
-    if (!aligned16(out) || !strides_vectorizable(plan->geo)) return DA2_ERR_UNSUPPORTED;
+    if (!aligned16(out) || !out_strides_vectorizable(plan->geo)) return DA2_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const int out_fp32 = plan->cfg.out_dtype == DA2_OUT_FP32;
     if (hipError_t e = da2::launch_attention(plan->geo, plan->ws, workspace, out, out_fp32, s); e != hipSuccess)
@@ -132,7 +135,8 @@ extern "C" da2_status da2_forward_scratch(const da2_plan_t* plan, const void* q,
                                           void* out, void* hip_stream) {
     if (!plan || !q || !k || !v || !out) return DA2_ERR_INVALID_ARG;
     if (plan->ws.total > DA2_SCRATCH_BYTES) return DA2_ERR_WORKSPACE;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !strides_vectorizable(plan->geo))
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !strides_vectorizable(plan->geo) ||
+        !out_strides_vectorizable(plan->geo))
         return DA2_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     void* ws = nullptr;

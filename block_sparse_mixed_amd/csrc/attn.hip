@@ -983,7 +983,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
         const int qs = 32 * wq + lq;
         const int64_t n = slot_raster(g, qp, qs);
         if (n >= 0) {
-            const int64_t rowoff = (int64_t)b * g.stride_b + (int64_t)h * g.stride_h + n * g.stride_n;
+            const int64_t rowoff = (int64_t)b * g.ostride_b + (int64_t)h * g.ostride_h + n * g.ostride_n;
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll

@@ -17,6 +17,7 @@ struct Geo {
     int32_t n_hi, n_lo;
     int64_t tokens;
     int64_t stride_b, stride_h, stride_n;
+    int64_t ostride_b, ostride_h, ostride_n;   // of out
     double tau;
 };
 

@@ -26,6 +26,7 @@ extern "C" da2_status da2_plan(const da2_config* cfg, da2_plan_t** out) {
         return DA2_ERR_INVALID_ARG;
     if (!(c.softmax_scale >= 0.0) || !std::isfinite(c.softmax_scale)) return DA2_ERR_INVALID_ARG;
     if (c.stride_b < 0 || c.stride_h < 0 || c.stride_n < 0) return DA2_ERR_INVALID_ARG;
+    if (c.out_stride_b < 0 || c.out_stride_h < 0 || c.out_stride_n < 0) return DA2_ERR_INVALID_ARG;
     if (c.head_dim % 32 != 0 || c.head_dim > DA2_DPAD) return DA2_ERR_UNSUPPORTED;
     if ((int64_t)c.win_h * c.win_w > DA2_TILE) return DA2_ERR_UNSUPPORTED;
 
@@ -82,6 +83,16 @@ extern "C" da2_status da2_plan(const da2_config* cfg, da2_plan_t** out) {
         g.stride_n = c.stride_n;
         g.stride_h = c.stride_h;
         g.stride_b = c.stride_b;
+    }
+    if (c.out_stride_b == 0 && c.out_stride_h == 0 && c.out_stride_n == 0) {
+        g.ostride_b = g.stride_b;
+        g.ostride_h = g.stride_h;
+        g.ostride_n = g.stride_n;
+    } else {
+        if (c.out_stride_n < c.head_dim || c.out_stride_h <= 0 || c.out_stride_b <= 0) return DA2_ERR_INVALID_ARG;
+        g.ostride_b = c.out_stride_b;
+        g.ostride_h = c.out_stride_h;
+        g.ostride_n = c.out_stride_n;
     }
     g.tau = c.softmax_scale > 0.0 ? c.softmax_scale : 1.0 / std::sqrt((double)c.head_dim);
 

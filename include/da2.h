@@ -22,12 +22,13 @@
  *    da2_forward_scratch, whose workspace is a static device array of the
  *    library shared by all its calls on a GPU (see there).
  *  - Tensors q, k, v, out are [batch, heads, tokens, head_dim] addressed by
- *    element strides (stride_b, stride_h, stride_n), head_dim contiguous.
+ *    element strides (stride_b, stride_h, stride_n; out may have its own,
+ *    out_stride_*), head_dim contiguous.
  *    Tokens are in raster order (frame, row, column) of a frames x grid_h x
  *    grid_w latent grid. q, k, v are bf16; out is bf16 or fp32.
  *  - Rows are read and written as 16-byte vectors: the q, k, v and out
- *    pointers must be 16-byte aligned and the three strides multiples of 8
- *    elements; otherwise da2_prepare / da2_attention return
+ *    pointers must be 16-byte aligned and the strides (inputs' and out's)
+ *    multiples of 8 elements; otherwise da2_prepare / da2_attention return
  *    DA2_ERR_UNSUPPORTED before enqueuing anything.
  *  - Every call that takes a workspace also takes its size in bytes
  *    (workspace_bytes): a buffer smaller than the plan's workspace_bytes, or
@@ -100,6 +101,9 @@ typedef struct da2_config {
     int64_t stride_n;
     int32_t out_dtype;        /* DA2_OUT_BF16 or DA2_OUT_FP32 */
     uint32_t flags;           /* 0 or DA2_FLAG_PACK_EDGES; other bits are invalid */
+    int64_t out_stride_b;     /* element strides of out; all three 0 selects the */
+    int64_t out_stride_h;     /* strides of q, k, v (so a fused QKV input can   */
+    int64_t out_stride_n;     /* feed an output in another layout, e.g. [B,N,H,d]) */
 } da2_config;
 
 typedef struct da2_plan_s da2_plan_t;
@@ -151,7 +155,7 @@ typedef struct da2_plan_info_s {
 /* Validate cfg and build a plan. Host only: touches no GPU state.
  * Errors: DA2_ERR_INVALID_ARG for a NULL argument, a non-positive size,
  * negative strides (or stride_n < head_dim, or a zero stride_b / stride_h
- * when any stride is given), budgets outside [0, 1] or not finite, a
+ * when any stride is given; the same for the out_stride_* triple), budgets outside [0, 1] or not finite, a
  * negative or non-finite softmax_scale, an unknown out_dtype or flag bit,
  * or n_ret = 0; DA2_ERR_UNSUPPORTED for a head_dim or window outside the
  * domains above, more than DA2_MAX_BLOCKS blocks, or batch * heads > 65535.
