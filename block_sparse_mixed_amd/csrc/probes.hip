@@ -1,0 +1,292 @@
+// Hardware probes behind the kernels' design (gfx950): exactness of the
+// conversions and MFMAs the kernels rely on, and issue costs of the
+// instructions the attention kernel is built from. Not part of the product
+// path: test and measurement infrastructure, built into libda2_probes.so.
+//
+// Every entry point takes device buffers sized as stated, launches one small
+// kernel on the null stream, synchronises and returns the HIP error code.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// out[4 c + p] = bf16 bits of E4M3 code c widened from byte position p (0..3)
+__global__ void k_widen_fp8(uint16_t* out) {
+    const int c = threadIdx.x;   // 256 threads
+    const int word = c | (c << 8) | (c << 16) | (c << 24);
+    const v2bf lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false);
+    const v2bf hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true);
+    out[4 * c] = __builtin_bit_cast(uint16_t, lo[0]);
+    out[4 * c + 1] = __builtin_bit_cast(uint16_t, lo[1]);
+    out[4 * c + 2] = __builtin_bit_cast(uint16_t, hi[0]);
+    out[4 * c + 3] = __builtin_bit_cast(uint16_t, hi[1]);
+}
+
+// out[i] = E4M3 code of in[i] (v_cvt_pk_fp8_f32)
+__global__ void k_to_fp8(const float* in, uint8_t* out, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (2 * i + 1 >= n + 1) return;
+    const float a = in[2 * i];
+    const float b = 2 * i + 1 < n ? in[2 * i + 1] : 0.0f;
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    out[2 * i] = (uint8_t)(w & 0xFF);
+    if (2 * i + 1 < n) out[2 * i + 1] = (uint8_t)((w >> 8) & 0xFF);
+}
+
+// out[i] = E2M1 code of in[i] (v_cvt_scalef32_pk_fp4_f32 with scale 1)
+__global__ void k_to_fp4(const float* in, uint8_t* out, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (2 * i + 1 >= n + 1) return;
+    const float a = in[2 * i];
+    const float b = 2 * i + 1 < n ? in[2 * i + 1] : 0.0f;
+    const uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0);
+    out[2 * i] = (uint8_t)(w & 0xF);
+    if (2 * i + 1 < n) out[2 * i + 1] = (uint8_t)((w >> 4) & 0xF);
+}
+
+// One 32x32x64 MFMA with E4M3 operands and unit scales: D[r][c] = sum_k
+// A[r][k] B[k][c]. a, b: [32][64] codes (row r of A, column c of B, k
+// contiguous); d: [32][32] fp32. One wave.
+__global__ void k_mfma_fp8(const uint8_t* a, const uint8_t* b, float* d) {
+    const int l = threadIdx.x;
+    const int r = l & 31, h = l >> 5;
+    // lane l holds row/column l % 32 for k = 32 h .. 32 h + 31
+    v8i va, vb;
+    for (int i = 0; i < 8; ++i) {
+        va[i] = *reinterpret_cast<const int*>(a + r * 64 + 32 * h + 4 * i);
+        vb[i] = *reinterpret_cast<const int*>(b + r * 64 + 32 * h + 4 * i);
+    }
+    v16f acc = {};
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc, 0, 0, 0, 127, 0, 127);
+    // D element j of lane l: row 8 (j / 4) + 4 h + j % 4, column l % 32
+    for (int j = 0; j < 16; ++j) d[(8 * (j >> 2) + 4 * h + (j & 3)) * 32 + r] = acc[j];
+}
+
+// The same product with both operands widened to bf16 and four 32x32x16 bf16 MFMAs.
+__global__ void k_mfma_bf16_of_fp8(const uint8_t* a, const uint8_t* b, float* d) {
+    const int l = threadIdx.x;
+    const int r = l & 31, h = l >> 5;
+    v16f acc = {};
+    for (int s = 0; s < 4; ++s) {          // k = 16 s .. 16 s + 15; lane half h holds 8 of them
+        v8bf va, vb;
+        for (int i = 0; i < 4; ++i) {
+            const int k = 16 * s + 8 * h + 2 * i;
+            const int wa = a[r * 64 + k] | (a[r * 64 + k + 1] << 8);
+            const int wb = b[r * 64 + k] | (b[r * 64 + k + 1] << 8);
+            const v2bf xa = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wa, 1.0f, false);
+            const v2bf xb = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wb, 1.0f, false);
+            va[2 * i] = xa[0];
+            va[2 * i + 1] = xa[1];
+            vb[2 * i] = xb[0];
+            vb[2 * i + 1] = xb[1];
+        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, vb, acc, 0, 0, 0);
+    }
+    for (int j = 0; j < 16; ++j) d[(8 * (j >> 2) + 4 * h + (j & 3)) * 32 + r] = acc[j];
+}
+
+// ---- issue costs with one or two waves per SIMD ----
+// cyc[wave] = shader clocks for kIters iterations of a block of kN
+// instructions of one kind (independent chains), per wave.
+constexpr int kIters = 2048;
+constexpr int kN = 16;
+
+template <int KIND>
+__device__ __forceinline__ void block(float (&f)[8], int (&iv)[8], v16f (&acc)[4], const v8i& oa, const v8bf& ob) {
+#pragma unroll
+    for (int t = 0; t < kN; ++t) {
+        const int c = t & 7;
+        if constexpr (KIND == 0) f[c] = __builtin_fmaf(f[c], 1.0001f, 0.5f);
+        if constexpr (KIND == 1) f[c] = __builtin_amdgcn_exp2f(f[c]);
+        if constexpr (KIND == 2) iv[c] = __builtin_amdgcn_cvt_pk_fp8_f32(f[c], f[(c + 1) & 7], iv[c], false);
+        if constexpr (KIND == 3)
+            iv[c] = (int)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32((uint32_t)iv[c], f[c], f[(c + 1) & 7], 1.0f, 0);
+        if constexpr (KIND == 4) {
+            const v2bf x = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(iv[c], 1.0f, false);
+            iv[c] ^= __builtin_bit_cast(int, x);
+        }
+        // MFMAs: four independent accumulator chains
+        if constexpr (KIND == 5) acc[t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ob, ob, acc[t & 3], 0, 0, 0);
+        if constexpr (KIND == 6)
+            acc[t & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(oa, oa, acc[t & 3], 0, 0, 0, 127, 0, 127);
+        if constexpr (KIND == 7)
+            acc[t & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(oa, oa, acc[t & 3], 4, 4, 0, 127, 0, 127);
+    }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(512) void k_issue(float* sink, long long* cyc) {
+    const int lane = threadIdx.x & 63;
+    float f[8];
+    int iv[8];
+    for (int i = 0; i < 8; ++i) {
+        f[i] = 0.01f * (lane + i);
+        iv[i] = lane * 7 + i;
+    }
+    v16f acc[4] = {};
+    v8i oa;
+    v8bf ob;
+    for (int i = 0; i < 8; ++i) {
+        oa[i] = 0x38383838 ^ (lane & 1);
+        ob[i] = (__bf16)(1.0f / (1 + i));
+    }
+    __syncthreads();
+    const long long t0 = clock64();
+    for (int it = 0; it < kIters; ++it) block<KIND>(f, iv, acc, oa, ob);
+    const long long t1 = clock64();
+    float s = acc[0][0] + acc[1][1] + acc[2][2] + acc[3][3];
+    for (int i = 0; i < 8; ++i) s += f[i] + (float)iv[i];
+    sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+    if (lane == 0) cyc[blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = t1 - t0;
+}
+
+template <class K>
+hipError_t run_issue(K kern, int waves_per_simd, float* sink, long long* cyc) {
+    // 256 workgroups of 4 or 8 waves; 96 KiB of (unused) dynamic LDS each
+    // keeps them one per CU, so a SIMD holds 1 or 2 waves. sink and cyc are
+    // sized by the caller for 256 x 512 threads and 256 x 8 waves.
+    hipLaunchKernelGGL(kern, dim3(256), dim3(64 * 4 * waves_per_simd), 96 * 1024, 0, sink, cyc);
+    return hipDeviceSynchronize();
+}
+
+// ---- issue cost of memory instructions next to independent VALU work ----
+// One wave per SIMD. Per iteration: eight memory instructions of one kind and
+// 8 x 16 independent FMAs; mode 0: FMAs only; 1, 2, 3: each memory
+// instruction followed by 16 FMAs (1: global_load_dwordx4 into registers,
+// 2: global_load_lds_dwordx4 (LDS DMA), 3: ds_write_b128); 4, 5, 6: the
+// eight memory instructions back to back, then the FMAs.
+constexpr int kMemIters = 512;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void k_mem(const uint4* __restrict__ src, float* out, long long* cyc) {
+    extern __shared__ __align__(16) uint8_t lds[];          // 32 KiB used
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    float a[8];
+    for (int i = 0; i < 8; ++i) a[i] = threadIdx.x * 0.001f + i;
+    uint4 acc = {0, 0, 0, 0};
+    // each wave reads its own 8 KiB: src has 256 x 4 x 512 + 64 uint4
+    const uint4* base = src + ((size_t)blockIdx.x * 4 + w) * 512 + lane;
+    uint8_t* lbase = lds + w * 8192;
+    __syncthreads();
+    const long long t0 = clock64();
+    for (int it = 0; it < kMemIters; ++it) {
+        uint4 r[8];
+        if constexpr (MODE >= 4) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if constexpr (MODE == 4) r[j] = base[j * 64];
+                if constexpr (MODE == 5)
+                    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + j * 64),
+                                                     (__attribute__((address_space(3))) void*)(lbase + j * 1024), 16, 0, 0);
+                if constexpr (MODE == 6) *reinterpret_cast<uint4*>(lbase + j * 1024 + lane * 16) = make_uint4(it, j, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if constexpr (MODE == 1) r[j] = base[j * 64];
+            if constexpr (MODE == 2)
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + j * 64),
+                                                 (__attribute__((address_space(3))) void*)(lbase + j * 1024), 16, 0, 0);
+            if constexpr (MODE == 3) *reinterpret_cast<uint4*>(lbase + j * 1024 + lane * 16) = make_uint4(it, j, 0, 0);
+            if constexpr (MODE >= 1 && MODE <= 3) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) a[i] = __builtin_fmaf(a[i], 1.0001f, 0.5f);
+            if constexpr (MODE >= 1 && MODE <= 3) __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (MODE == 1 || MODE == 4) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc.x ^= r[j].x ^ r[j].w;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    const long long t1 = clock64();
+    float s = 0;
+    for (int i = 0; i < 8; ++i) s += a[i];
+    out[blockIdx.x * 256 + threadIdx.x] = s + acc.x + lds[threadIdx.x];
+    if (lane == 0) cyc[blockIdx.x * 4 + w] = t1 - t0;
+}
+
+}  // namespace
+
+extern "C" {
+
+// mode 0..6 as above. src: device uint4[256 * 4 * 512 + 64]; out: device
+// float[256 * 256]; cyc: device int64[256 * 4]. cyc holds clocks for 512
+// iterations (8 memory instructions and 128 FMAs each) per wave.
+int da2p_mem_issue(int mode, const void* src, float* out, long long* cyc) {
+    const uint4* s = static_cast<const uint4*>(src);
+    const size_t lds = 96 * 1024;                 // one workgroup per CU
+    switch (mode) {
+        case 0: hipLaunchKernelGGL(k_mem<0>, dim3(256), dim3(256), lds, 0, s, out, cyc); break;
+        case 1: hipLaunchKernelGGL(k_mem<1>, dim3(256), dim3(256), lds, 0, s, out, cyc); break;
+        case 2: hipLaunchKernelGGL(k_mem<2>, dim3(256), dim3(256), lds, 0, s, out, cyc); break;
+        case 3: hipLaunchKernelGGL(k_mem<3>, dim3(256), dim3(256), lds, 0, s, out, cyc); break;
+        case 4: hipLaunchKernelGGL(k_mem<4>, dim3(256), dim3(256), lds, 0, s, out, cyc); break;
+        case 5: hipLaunchKernelGGL(k_mem<5>, dim3(256), dim3(256), lds, 0, s, out, cyc); break;
+        case 6: hipLaunchKernelGGL(k_mem<6>, dim3(256), dim3(256), lds, 0, s, out, cyc); break;
+        default: return -1;
+    }
+    return (int)hipDeviceSynchronize();
+}
+
+
+// out: device uint16[1024]
+int da2p_widen_fp8(uint16_t* out) {
+    hipLaunchKernelGGL(k_widen_fp8, dim3(1), dim3(256), 0, 0, out);
+    return (int)hipDeviceSynchronize();
+}
+
+// in: device float[n], out: device uint8[n]
+int da2p_to_fp8(const float* in, uint8_t* out, int n) {
+    const int pairs = (n + 1) / 2;
+    hipLaunchKernelGGL(k_to_fp8, dim3((pairs + 255) / 256), dim3(256), 0, 0, in, out, n);
+    return (int)hipDeviceSynchronize();
+}
+
+// in: device float[n], out: device uint8[n] (one E2M1 code per byte)
+int da2p_to_fp4(const float* in, uint8_t* out, int n) {
+    const int pairs = (n + 1) / 2;
+    hipLaunchKernelGGL(k_to_fp4, dim3((pairs + 255) / 256), dim3(256), 0, 0, in, out, n);
+    return (int)hipDeviceSynchronize();
+}
+
+// a, b: device uint8[32 * 64] (E4M3 codes, k contiguous); d: device float[32 * 32]
+int da2p_mfma_fp8(const uint8_t* a, const uint8_t* b, float* d, int bf16_path) {
+    if (bf16_path)
+        hipLaunchKernelGGL(k_mfma_bf16_of_fp8, dim3(1), dim3(64), 0, 0, a, b, d);
+    else
+        hipLaunchKernelGGL(k_mfma_fp8, dim3(1), dim3(64), 0, 0, a, b, d);
+    return (int)hipDeviceSynchronize();
+}
+
+// kind: 0 v_fma_f32, 1 v_exp_f32, 2 v_cvt_pk_fp8_f32, 3 v_cvt_scalef32_pk_fp4_f32,
+// 4 v_cvt_scalef32_pk_bf16_fp8, 5 mfma bf16 32x32x16, 6 mfma scaled fp8 32x32x64,
+// 7 mfma scaled fp4 32x32x64; waves_per_simd 1 or 2.
+// sink: device float[256 * 512]; cyc: device int64[256 * 8] (per wave).
+// Returns the HIP error; cyc holds clocks for 2048 x 16 instructions per wave.
+int da2p_issue(int kind, int waves_per_simd, float* sink, long long* cyc) {
+    if (waves_per_simd != 1 && waves_per_simd != 2) return -1;
+    switch (kind) {
+        case 0: return (int)run_issue(k_issue<0>, waves_per_simd, sink, cyc);
+        case 1: return (int)run_issue(k_issue<1>, waves_per_simd, sink, cyc);
+        case 2: return (int)run_issue(k_issue<2>, waves_per_simd, sink, cyc);
+        case 3: return (int)run_issue(k_issue<3>, waves_per_simd, sink, cyc);
+        case 4: return (int)run_issue(k_issue<4>, waves_per_simd, sink, cyc);
+        case 5: return (int)run_issue(k_issue<5>, waves_per_simd, sink, cyc);
+        case 6: return (int)run_issue(k_issue<6>, waves_per_simd, sink, cyc);
+        case 7: return (int)run_issue(k_issue<7>, waves_per_simd, sink, cyc);
+        default: return -1;
+    }
+}
+
+}  // extern "C"

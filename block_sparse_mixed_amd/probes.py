@@ -1,0 +1,143 @@
+"""Hardware probes behind the design of the kernels (gfx950), run through
+libda2_probes.so. Test and measurement infrastructure, not the product path.
+
+    python -m block_sparse_mixed_amd.probes     prints the issue-cost table and
+                                                the exactness summaries (needs a GPU)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+PROBE_LIB = os.path.join(_HERE, "lib", "libda2_probes.so")
+_lib = None
+
+KINDS = {0: "v_fma_f32", 1: "v_exp_f32", 2: "v_cvt_pk_fp8_f32 (2 values)", 3: "v_cvt_scalef32_pk_fp4_f32 (2 values)",
+         4: "v_cvt_scalef32_pk_bf16_fp8 (2 values)", 5: "v_mfma_f32_32x32x16_bf16",
+         6: "v_mfma_scale_f32_32x32x64_f8f6f4 (fp8)", 7: "v_mfma_scale_f32_32x32x64_f8f6f4 (fp4)"}
+ITERS, PER_ITER = 2048, 16
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(PROBE_LIB):
+            raise ImportError(f"{PROBE_LIB} is missing: build it with `python -m block_sparse_mixed_amd.build`")
+        _lib = ctypes.CDLL(PROBE_LIB)
+        P = ctypes.c_void_p
+        _lib.da2p_widen_fp8.argtypes = [P]
+        _lib.da2p_to_fp8.argtypes = [P, P, ctypes.c_int]
+        _lib.da2p_to_fp4.argtypes = [P, P, ctypes.c_int]
+        _lib.da2p_mfma_fp8.argtypes = [P, P, P, ctypes.c_int]
+        _lib.da2p_issue.argtypes = [ctypes.c_int, ctypes.c_int, P, P]
+        _lib.da2p_mem_issue.argtypes = [ctypes.c_int, P, P, P]
+    return _lib
+
+
+def _ok(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"{what}: HIP error {rc}")
+
+
+def widen_fp8():
+    """bf16 bit patterns [256 codes][4 byte positions] from v_cvt_scalef32_pk_bf16_fp8."""
+    import torch
+    out = torch.empty(1024, dtype=torch.int16, device="cuda")
+    _ok(lib().da2p_widen_fp8(out.data_ptr()), "widen_fp8")
+    return out.cpu().numpy().view(np.uint16).reshape(256, 4)
+
+
+def to_fp8(x: np.ndarray) -> np.ndarray:
+    """E4M3 codes of float32 values from v_cvt_pk_fp8_f32."""
+    import torch
+    xi = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    out = torch.empty(xi.numel(), dtype=torch.uint8, device="cuda")
+    _ok(lib().da2p_to_fp8(xi.data_ptr(), out.data_ptr(), xi.numel()), "to_fp8")
+    return out.cpu().numpy()
+
+
+def to_fp4(x: np.ndarray) -> np.ndarray:
+    """E2M1 codes (one per byte) of float32 values from v_cvt_scalef32_pk_fp4_f32, scale 1."""
+    import torch
+    xi = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    out = torch.empty(xi.numel(), dtype=torch.uint8, device="cuda")
+    _ok(lib().da2p_to_fp4(xi.data_ptr(), out.data_ptr(), xi.numel()), "to_fp4")
+    return out.cpu().numpy()
+
+
+def mfma_fp8(a_codes: np.ndarray, b_codes: np.ndarray, bf16_path: bool) -> np.ndarray:
+    """D = A B for E4M3 code matrices A [32][64], B^T [32][64] (k contiguous),
+    on one scaled f8f6f4 MFMA, or on bf16 MFMAs over the exactly widened codes."""
+    import torch
+    a = torch.from_numpy(np.ascontiguousarray(a_codes, dtype=np.uint8)).cuda()
+    b = torch.from_numpy(np.ascontiguousarray(b_codes, dtype=np.uint8)).cuda()
+    d = torch.empty(32 * 32, dtype=torch.float32, device="cuda")
+    _ok(lib().da2p_mfma_fp8(a.data_ptr(), b.data_ptr(), d.data_ptr(), int(bf16_path)), "mfma_fp8")
+    return d.cpu().numpy().reshape(32, 32)
+
+
+# flops per MFMA instruction of kinds 5, 6, 7
+MFMA_FLOP = {5: 2 * 32 * 32 * 16, 6: 2 * 32 * 32 * 64, 7: 2 * 32 * 32 * 64}
+
+
+def issue_cycles(kind: int, waves_per_simd: int):
+    """(clock-counter ticks per instruction of one kind per wave, averaged over
+    the launch; wall seconds of the launch) for one workgroup per CU and 1 or
+    2 waves per SIMD (256 workgroups)."""
+    import time
+
+    import torch
+    sink = torch.empty(256 * 512, dtype=torch.float32, device="cuda")
+    cyc = torch.zeros(256 * 8, dtype=torch.int64, device="cuda")
+    _ok(lib().da2p_issue(kind, waves_per_simd, sink.data_ptr(), cyc.data_ptr()), "issue")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _ok(lib().da2p_issue(kind, waves_per_simd, sink.data_ptr(), cyc.data_ptr()), "issue")   # synchronises
+    wall = time.perf_counter() - t0
+    c = cyc.cpu().numpy()[: 256 * 4 * waves_per_simd]
+    return float(c.mean()) / (ITERS * PER_ITER), wall
+
+
+MEM_MODES = {0: "16 FMAs only", 1: "global_load_dwordx4 + 16 FMAs", 2: "global_load_lds_dwordx4 + 16 FMAs",
+             3: "ds_write_b128 + 16 FMAs", 4: "global_load_dwordx4, 8 back to back", 5: "global_load_lds_dwordx4, 8 back to back",
+             6: "ds_write_b128, 8 back to back"}
+
+
+def mem_issue_cycles(mode: int) -> float:
+    """Clocks per (memory instruction + 16 FMAs), one wave per SIMD, per wave."""
+    import torch
+    src = torch.zeros(256 * 4 * 512 + 64, 4, dtype=torch.int32, device="cuda")
+    out = torch.empty(256 * 256, dtype=torch.float32, device="cuda")
+    cyc = torch.zeros(256 * 4, dtype=torch.int64, device="cuda")
+    for _ in range(2):
+        _ok(lib().da2p_mem_issue(mode, src.data_ptr(), out.data_ptr(), cyc.data_ptr()), "mem_issue")
+    return float(cyc.cpu().numpy().mean()) / (512 * 8)
+
+
+def main():
+    import torch
+    print(f"device: {torch.cuda.get_device_name(0)}")
+    print("\nticks: clock-counter ticks (shader cycles) per instruction with one wave per SIMD;")
+    print("two waves: the same instruction stream in two waves per SIMD, as ticks per instruction")
+    print("per SIMD from the wall-time ratio of the two launches (ticks_1 * wall_2 / (2 * wall_1)).")
+    print("\n| instruction | ticks, 1 wave/SIMD | ticks per instruction per SIMD, 2 waves | TFLOP/s, 1 / 2 waves |")
+    print("|---|---|---|---|")
+    for k, name in KINDS.items():
+        t1, w1 = issue_cycles(k, 1)
+        _, w2 = issue_cycles(k, 2)
+        n1 = 256 * 4 * ITERS * PER_ITER
+        tf = f"{n1 * MFMA_FLOP[k] / w1 / 1e12:.0f} / {2 * n1 * MFMA_FLOP[k] / w2 / 1e12:.0f}" if k in MFMA_FLOP else ""
+        print(f"| {name} | {t1:.1f} | {t1 * w2 / (2 * w1):.1f} | {tf} |")
+    print("\nmemory instructions among independent FMAs, one wave per SIMD (ticks per memory instruction")
+    print("and its 16 FMAs; the difference to the FMA-only row is the memory instruction's issue cost):")
+    print("\n| stream | ticks |")
+    print("|---|---|")
+    for mode, name in MEM_MODES.items():
+        print(f"| {name} | {mem_issue_cycles(mode):.1f} |")
+
+if __name__ == "__main__":
+    main()
