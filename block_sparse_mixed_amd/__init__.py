@@ -56,7 +56,7 @@ class PlanInfo(ctypes.Structure):
     ] + [(n, ctypes.c_uint64) for n in (
         "off_pool", "off_k8", "off_v8t", "off_e8", "off_q4", "off_k4", "off_v4t",
         "off_sq4", "off_sk4", "off_sv4t", "off_scores", "off_labels", "off_hi", "off_lo", "off_status",
-        "off_qb", "off_bias")] + [("n_full", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+        "off_q8", "off_bias")] + [("n_full", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -21,8 +21,8 @@
 //   a SIMD are therefore always in opposite halves of their work: one feeds
 //   the matrix pipe while the other exponentiates.
 //     S^T = K . Q^T        fp8 tiles: V_MFMA_F32_32X32X16_BF16 on the E4M3
-//                          values widened to bf16 (exact): Q once by the
-//                          preparation kernel, K in registers from the E4M3
+//                          values widened to bf16 (exact): Q once per
+//                          workgroup into LDS, K in registers from the E4M3
 //                          codes in LDS;
 //                          MXFP4 tiles: V_MFMA_SCALE_F32_32X32X64_F8F6F4
 //     softmax (base 2, integer running max per team, lane-local rescale)
@@ -711,17 +711,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
     const uint64_t qtile = (uint64_t)bh * nb + qb;
     const int n_tiles = g.n_hi + g.n_lo;
 
-    // The query block's Q operands (swizzled rows) go first: their DMA runs
-    // while the tile list below is gathered.
+    // The query block's Q operands go first: the E4M3 codes into registers
+    // (two 16-byte chunks a thread, widened to bf16 once the tile list below
+    // has been gathered) and the E2M1 codes and scales by DMA into LDS.
+    uint4 q8c[2];
     {
-        const uint8_t* qb_src = ws + a.L.qb + qtile * (DA2_TILE * DA2_DPAD * 2);
+        const uint8_t* q8_src = ws + a.L.q8 + qtile * (DA2_TILE * DA2_DPAD);
 #pragma unroll
-        for (int n = 0; n < 32 / kWaves; ++n) {       // 32 KiB: 32 rows of 1 KiB
-            const int wr = w + kWaves * n;
-            const int p = wr * 64 + lane;
-            const int q = p >> 4, pc = p & 15;
-            dma16(qb_src + (q * 16 + (pc ^ (q & 15))) * 16, qlds + kQb + wr * 1024);
-        }
+        for (int k = 0; k < 2; ++k) q8c[k] = *reinterpret_cast<const uint4*>(q8_src + (tid + kThreads * k) * 16);
         const uint8_t* q4_src = ws + a.L.q4 + qtile * (DA2_TILE * DA2_DPAD / 2);
 #pragma unroll
         for (int n = 0; n < 8 / kWaves; ++n) {      // 8 KiB: 8 rows
@@ -764,6 +761,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, const uint8_
                 tl[i] = (int32_t)e;
             }
         }
+    }
+    // Q as bf16 (exact widening of the E4M3 codes, without the block scale):
+    // 16-byte chunk c (8 channels) of query slot q at chunk c ^ (q & 15)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int ci = tid + kThreads * k;          // 16 codes: slot ci / 8, channels 16 (ci % 8) ..
+        const int q = ci >> 3, c = 2 * (ci & 7);
+        uint8_t* row = qlds + kQb + q * 256;
+        *reinterpret_cast<v8bf*>(row + ((c ^ (q & 15)) << 4)) = widen_e4m3(q8c[k].x, q8c[k].y);
+        *reinterpret_cast<v8bf*>(row + (((c + 1) ^ (q & 15)) << 4)) = widen_e4m3(q8c[k].z, q8c[k].w);
     }
     __syncthreads();
     // The first fp8 section's first K tile is fetched now, under the rest of

@@ -103,7 +103,7 @@ extern "C" da2_status da2_plan(const da2_config* cfg, da2_plan_t** out) {
     auto take = [&](uint64_t bytes) { uint64_t o = off; off = align256(off + bytes); return o; };
     L.pool = take(4 * B * N * P * 8);
     L.k8 = take(B * N * T * P);
-    L.qb = take(B * N * T * P * 2);
+    L.q8 = take(B * N * T * P);
     L.v8t = take(B * N * P * T);
     L.e8 = take(3 * B * N);
     L.q4 = take(B * N * T * P / 2);
@@ -163,7 +163,7 @@ extern "C" da2_status da2_plan_info(const da2_plan_t* plan, da2_plan_info_t* out
     i.off_hi = L.hi;
     i.off_lo = L.lo;
     i.off_status = L.status;
-    i.off_qb = L.qb;
+    i.off_q8 = L.q8;
     i.off_bias = L.bias;
     *out = i;
     return DA2_OK;

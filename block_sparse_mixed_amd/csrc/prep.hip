@@ -10,14 +10,12 @@
 // each window's bf16 rows once (8 rows of 16 consecutive raster tokens for an
 // 8x16 window), stages them in LDS and writes:
 //   - E4M3 codes with one power-of-two scale for the whole block
-//     (K slot-major; V channel-major so that PV can contract over slots),
-//     and for Q the same codes decoded to bf16 (scale-free, exact; the codes
-//     themselves are not stored),
+//     (Q, K slot-major; V channel-major so that PV can contract over slots),
 //   - MXFP4 codes with an E8M0 scale per 32 elements along the contraction
 //     axis (Q, K along channels; V along slots),
 //   - for Q and K, the per-channel mean (fp64, exact sum of bf16 values then
 //     one rounding) and maximum over the window's real tokens.
-// HBM-bound: ~2 bytes read and ~2.4 bytes written per element (the codes of
+// HBM-bound: ~2 bytes read and ~2 bytes written per element (the codes of
 // padded slots included).
 #include "common.hpp"
 
@@ -124,9 +122,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
 
     if (tz < 2) {
         // ---- row pass (Q, K): E4M3 slot-major and MXFP4 along channels ----
-        // (the Q codes are stored as their exact bf16 decode only)
-        uint8_t* c8 = a.ws + a.L.k8 + tileid * (DA2_TILE * DA2_DPAD);
-        uint16_t* cb = reinterpret_cast<uint16_t*>(a.ws + a.L.qb) + tileid * (DA2_TILE * DA2_DPAD);
+        uint8_t* c8 = a.ws + (tz == 0 ? a.L.q8 : a.L.k8) + tileid * (DA2_TILE * DA2_DPAD);
         uint8_t* c4 = a.ws + (tz == 0 ? a.L.q4 : a.L.k4) + tileid * (DA2_TILE * DA2_DPAD / 2);
         uint8_t* s4 = a.ws + (tz == 0 ? a.L.sq4 : a.L.sk4) + tileid * (DA2_TILE * DA2_DPAD / 32);
 #pragma unroll
@@ -147,15 +143,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
             uint2 o8;
             o8.x = pack_fp8x4(x[0] * inv8, x[1] * inv8, x[2] * inv8, x[3] * inv8);
             o8.y = pack_fp8x4(x[4] * inv8, x[5] * inv8, x[6] * inv8, x[7] * inv8);
-            if (tz == 1) *reinterpret_cast<uint2*>(c8 + s * DA2_DPAD + cc * 8) = o8;
-            if (tz == 0) {      // Q: its bf16 decode is the QK^T operand of the fp8 phase
-                uint4 ob;
-                ob.x = fp8x2_to_bf16x2<false>(o8.x);
-                ob.y = fp8x2_to_bf16x2<true>(o8.x);
-                ob.z = fp8x2_to_bf16x2<false>(o8.y);
-                ob.w = fp8x2_to_bf16x2<true>(o8.y);
-                *reinterpret_cast<uint4*>(cb + s * DA2_DPAD + cc * 8) = ob;
-            }
+            *reinterpret_cast<uint2*>(c8 + s * DA2_DPAD + cc * 8) = o8;
             // 32-channel group = 4 consecutive lanes
             gmax = max(gmax, (uint32_t)__shfl_xor((int)gmax, 1));
             gmax = max(gmax, (uint32_t)__shfl_xor((int)gmax, 2));

@@ -91,20 +91,9 @@ def check_prepare(run: GpuRun, bh: int, st: P.HeadState):
     for t, name in enumerate(("q", "k", "v")):
         assert np.array_equal(e8[t, bh], st.ops[name + "8_exp"]), f"{name} fp8 scale"
     for name in ("q", "k"):
-        if name == "q":
-            # the Q codes are stored as their bf16 decode, which is one-to-one
-            # on E4M3 (the sign of zero included): compare decoded values bit
-            # for bit, padding included (zero codes decode to +0)
-            cb = run.da2.workspace_section(run.plan, run.ws, "qb", torch.bfloat16, (BH, nb, T, T))[bh]
-            want = np.zeros((nb, T, T), dtype=np.uint8)
-            want[:, :bs, :d] = st.ops["q8"]
-            got_bits = cb.view(torch.int16).cpu().numpy()
-            want_bits = torch.from_numpy(F.decode_e4m3(want)).to(torch.bfloat16).view(torch.int16).numpy()
-            assert np.array_equal(got_bits, want_bits), "q fp8 codes (bf16 decode)"
-        else:
-            c8 = run.sec(name + "8", torch.uint8, (BH, nb, T, T))[bh]
-            assert np.array_equal(c8[:, :bs, :d], st.ops[name + "8"]), f"{name} fp8 codes"
-            assert not c8[:, bs:, :].any() and not c8[:, :, d:].any()
+        c8 = run.sec(name + "8", torch.uint8, (BH, nb, T, T))[bh]
+        assert np.array_equal(c8[:, :bs, :d], st.ops[name + "8"]), f"{name} fp8 codes"
+        assert not c8[:, bs:, :].any() and not c8[:, :, d:].any()
         c4 = unpack_nibbles(run.sec(name + "4", torch.uint8, (BH, nb, T, T // 2))[bh])
         assert np.array_equal(c4[:, :bs, :d], st.ops[name + "4"]), f"{name} mxfp4 codes"
         s4 = run.sec("s" + name + "4", torch.uint8, (BH, nb, T, 4))[bh].astype(int) - 127

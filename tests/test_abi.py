@@ -114,7 +114,7 @@ def test_workspace_layout_is_aligned_and_disjoint():
     i = p.info
     bh, nb, T, P = 12, 336, 128, 128
     sizes = {"pool": 4 * bh * nb * P * 8, "k8": bh * nb * T * P,
-             "qb": bh * nb * T * P * 2, "v8t": bh * nb * P * T,
+             "q8": bh * nb * T * P, "v8t": bh * nb * P * T,
              "e8": 3 * bh * nb, "q4": bh * nb * T * P // 2, "k4": bh * nb * T * P // 2, "v4t": bh * nb * P * T // 2,
              "sq4": bh * nb * T * 4, "sk4": bh * nb * T * 4, "sv4t": bh * nb * P * 4, "scores": 2 * bh * nb * nb * 8,
              "labels": bh * nb * nb, "hi": bh * nb * 50 * 4, "lo": bh * nb * 118 * 4, "status": 16,
