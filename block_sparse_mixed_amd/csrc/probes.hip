@@ -16,6 +16,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef short v2s __attribute__((ext_vector_type(2)));
 
 // out[4 c + p] = bf16 bits of E4M3 code c widened from byte position p (0..3)
 __global__ void k_widen_fp8(uint16_t* out) {
@@ -92,6 +93,39 @@ __global__ void k_mfma_bf16_of_fp8(const uint8_t* a, const uint8_t* b, float* d)
     for (int j = 0; j < 16; ++j) d[(8 * (j >> 2) + 4 * h + (j & 3)) * 32 + r] = acc[j];
 }
 
+// The same product on four unscaled 32x32x16 fp8 MFMAs over the codes as
+// they are (lane half h holds k = 16 s + 8 h .. + 7 of row / column l % 32).
+__global__ void k_mfma_fp8_k16(const uint8_t* a, const uint8_t* b, float* d) {
+    const int l = threadIdx.x;
+    const int r = l & 31, h = l >> 5;
+    v16f acc = {};
+    for (int s = 0; s < 4; ++s) {
+        const long va = *reinterpret_cast<const long*>(a + r * 64 + 16 * s + 8 * h);
+        const long vb = *reinterpret_cast<const long*>(b + r * 64 + 16 * s + 8 * h);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(va, vb, acc, 0, 0, 0);
+    }
+    for (int j = 0; j < 16; ++j) d[(8 * (j >> 2) + 4 * h + (j & 3)) * 32 + r] = acc[j];
+}
+
+// out[i] = E4M3 code (fmt 0) or E2M1 code (fmt 1, one per byte) of the bf16
+// value in[i] converted with v_cvt_scalef32_pk_fp8_bf16 / _fp4_bf16 and the
+// given scale operand; n even.
+__global__ void k_bf16_to(const uint32_t* in, float scale, uint8_t* out, int pairs, int fmt) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= pairs) return;
+    const v2bf x = __builtin_bit_cast(v2bf, in[i]);
+    if (fmt == 0) {
+        const v2s o = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16((v2s){0, 0}, x, scale, false);
+        const uint32_t w = __builtin_bit_cast(uint32_t, o);
+        out[2 * i] = (uint8_t)(w & 0xFF);
+        out[2 * i + 1] = (uint8_t)((w >> 8) & 0xFF);
+    } else {
+        const uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, x, scale, 0);
+        out[2 * i] = (uint8_t)(w & 0xF);
+        out[2 * i + 1] = (uint8_t)((w >> 4) & 0xF);
+    }
+}
+
 // ---- issue costs with one or two waves per SIMD ----
 // cyc[wave] = shader clocks for kIters iterations of a block of kN
 // instructions of one kind (independent chains), per wave.
@@ -118,6 +152,18 @@ __device__ __forceinline__ void block(float (&f)[8], int (&iv)[8], v16f (&acc)[4
             acc[t & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(oa, oa, acc[t & 3], 0, 0, 0, 127, 0, 127);
         if constexpr (KIND == 7)
             acc[t & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(oa, oa, acc[t & 3], 4, 4, 0, 127, 0, 127);
+        if constexpr (KIND == 8) {
+            const long o8 = ((long)oa[1] << 32) | (uint32_t)oa[0];
+            acc[t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(o8, o8, acc[t & 3], 0, 0, 0);
+        }
+        if constexpr (KIND == 9) {
+            const v2s o = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(v2s, iv[c]),
+                                                                    __builtin_bit_cast(v2bf, iv[(c + 1) & 7]), f[c], false);
+            iv[c] = __builtin_bit_cast(int, o);
+        }
+        if constexpr (KIND == 10)
+            iv[c] = (int)__builtin_amdgcn_cvt_scalef32_pk_fp4_bf16((uint32_t)iv[c], __builtin_bit_cast(v2bf, iv[(c + 1) & 7]),
+                                                                   f[c], 0);
     }
 }
 
@@ -261,17 +307,33 @@ int da2p_to_fp4(const float* in, uint8_t* out, int n) {
 }
 
 // a, b: device uint8[32 * 64] (E4M3 codes, k contiguous); d: device float[32 * 32]
-int da2p_mfma_fp8(const uint8_t* a, const uint8_t* b, float* d, int bf16_path) {
-    if (bf16_path)
+// path 0: one scaled f8f6f4 32x32x64 MFMA; 1: bf16 MFMAs over the widened
+// codes; 2: four unscaled fp8 32x32x16 MFMAs
+int da2p_mfma_fp8(const uint8_t* a, const uint8_t* b, float* d, int path) {
+    if (path == 1)
         hipLaunchKernelGGL(k_mfma_bf16_of_fp8, dim3(1), dim3(64), 0, 0, a, b, d);
-    else
+    else if (path == 2)
+        hipLaunchKernelGGL(k_mfma_fp8_k16, dim3(1), dim3(64), 0, 0, a, b, d);
+    else if (path == 0)
         hipLaunchKernelGGL(k_mfma_fp8, dim3(1), dim3(64), 0, 0, a, b, d);
+    else
+        return -1;
+    return (int)hipDeviceSynchronize();
+}
+
+// in: device uint16[n] (bf16 bits, n even); out: device uint8[n]; fmt 0: E4M3, 1: E2M1
+int da2p_bf16_to(const uint16_t* in, float scale, uint8_t* out, int n, int fmt) {
+    if (n % 2 || fmt < 0 || fmt > 1) return -1;
+    const int pairs = n / 2;
+    hipLaunchKernelGGL(k_bf16_to, dim3((pairs + 255) / 256), dim3(256), 0, 0, reinterpret_cast<const uint32_t*>(in),
+                       scale, out, pairs, fmt);
     return (int)hipDeviceSynchronize();
 }
 
 // kind: 0 v_fma_f32, 1 v_exp_f32, 2 v_cvt_pk_fp8_f32, 3 v_cvt_scalef32_pk_fp4_f32,
 // 4 v_cvt_scalef32_pk_bf16_fp8, 5 mfma bf16 32x32x16, 6 mfma scaled fp8 32x32x64,
-// 7 mfma scaled fp4 32x32x64; waves_per_simd 1 or 2.
+// 7 mfma scaled fp4 32x32x64, 8 mfma fp8 32x32x16 (unscaled), 9
+// v_cvt_scalef32_pk_fp8_bf16, 10 v_cvt_scalef32_pk_fp4_bf16; waves_per_simd 1 or 2.
 // sink: device float[256 * 512]; cyc: device int64[256 * 8] (per wave).
 // Returns the HIP error; cyc holds clocks for 2048 x 16 instructions per wave.
 int da2p_issue(int kind, int waves_per_simd, float* sink, long long* cyc) {
@@ -285,6 +347,9 @@ int da2p_issue(int kind, int waves_per_simd, float* sink, long long* cyc) {
         case 5: return (int)run_issue(k_issue<5>, waves_per_simd, sink, cyc);
         case 6: return (int)run_issue(k_issue<6>, waves_per_simd, sink, cyc);
         case 7: return (int)run_issue(k_issue<7>, waves_per_simd, sink, cyc);
+        case 8: return (int)run_issue(k_issue<8>, waves_per_simd, sink, cyc);
+        case 9: return (int)run_issue(k_issue<9>, waves_per_simd, sink, cyc);
+        case 10: return (int)run_issue(k_issue<10>, waves_per_simd, sink, cyc);
         default: return -1;
     }
 }

@@ -18,7 +18,9 @@ _lib = None
 
 KINDS = {0: "v_fma_f32", 1: "v_exp_f32", 2: "v_cvt_pk_fp8_f32 (2 values)", 3: "v_cvt_scalef32_pk_fp4_f32 (2 values)",
          4: "v_cvt_scalef32_pk_bf16_fp8 (2 values)", 5: "v_mfma_f32_32x32x16_bf16",
-         6: "v_mfma_scale_f32_32x32x64_f8f6f4 (fp8)", 7: "v_mfma_scale_f32_32x32x64_f8f6f4 (fp4)"}
+         6: "v_mfma_scale_f32_32x32x64_f8f6f4 (fp8)", 7: "v_mfma_scale_f32_32x32x64_f8f6f4 (fp4)",
+         8: "v_mfma_f32_32x32x16_fp8_fp8", 9: "v_cvt_scalef32_pk_fp8_bf16 (2 values)",
+         10: "v_cvt_scalef32_pk_fp4_bf16 (2 values)"}
 ITERS, PER_ITER = 2048, 16
 
 
@@ -33,6 +35,7 @@ def lib():
         _lib.da2p_to_fp8.argtypes = [P, P, ctypes.c_int]
         _lib.da2p_to_fp4.argtypes = [P, P, ctypes.c_int]
         _lib.da2p_mfma_fp8.argtypes = [P, P, P, ctypes.c_int]
+        _lib.da2p_bf16_to.argtypes = [P, ctypes.c_float, P, ctypes.c_int, ctypes.c_int]
         _lib.da2p_issue.argtypes = [ctypes.c_int, ctypes.c_int, P, P]
         _lib.da2p_mem_issue.argtypes = [ctypes.c_int, P, P, P]
     return _lib
@@ -69,19 +72,37 @@ def to_fp4(x: np.ndarray) -> np.ndarray:
     return out.cpu().numpy()
 
 
-def mfma_fp8(a_codes: np.ndarray, b_codes: np.ndarray, bf16_path: bool) -> np.ndarray:
+MFMA_PATHS = {"f8f6f4": 0, "bf16": 1, "fp8_k16": 2}
+
+
+def bf16_to(x_bits: np.ndarray, scale: float, fmt: str) -> np.ndarray:
+    """E4M3 (fmt "fp8") or E2M1 (fmt "fp4", one code per byte) codes of bf16
+    values (uint16 bit patterns, even count) from v_cvt_scalef32_pk_fp8_bf16 /
+    v_cvt_scalef32_pk_fp4_bf16 with the given scale operand."""
+    import torch
+    xb = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    if xb.size % 2:
+        raise ValueError("an even number of values")
+    xi = torch.from_numpy(xb.view(np.int16)).cuda()
+    out = torch.empty(xb.size, dtype=torch.uint8, device="cuda")
+    _ok(lib().da2p_bf16_to(xi.data_ptr(), float(scale), out.data_ptr(), xb.size, {"fp8": 0, "fp4": 1}[fmt]), "bf16_to")
+    return out.cpu().numpy()
+
+
+def mfma_fp8(a_codes: np.ndarray, b_codes: np.ndarray, path: str) -> np.ndarray:
     """D = A B for E4M3 code matrices A [32][64], B^T [32][64] (k contiguous),
-    on one scaled f8f6f4 MFMA, or on bf16 MFMAs over the exactly widened codes."""
+    on one scaled f8f6f4 MFMA ("f8f6f4"), on bf16 MFMAs over the exactly
+    widened codes ("bf16"), or on four unscaled 32x32x16 fp8 MFMAs ("fp8_k16")."""
     import torch
     a = torch.from_numpy(np.ascontiguousarray(a_codes, dtype=np.uint8)).cuda()
     b = torch.from_numpy(np.ascontiguousarray(b_codes, dtype=np.uint8)).cuda()
     d = torch.empty(32 * 32, dtype=torch.float32, device="cuda")
-    _ok(lib().da2p_mfma_fp8(a.data_ptr(), b.data_ptr(), d.data_ptr(), int(bf16_path)), "mfma_fp8")
+    _ok(lib().da2p_mfma_fp8(a.data_ptr(), b.data_ptr(), d.data_ptr(), MFMA_PATHS[path]), "mfma_fp8")
     return d.cpu().numpy().reshape(32, 32)
 
 
-# flops per MFMA instruction of kinds 5, 6, 7
-MFMA_FLOP = {5: 2 * 32 * 32 * 16, 6: 2 * 32 * 32 * 64, 7: 2 * 32 * 32 * 64}
+# flops per MFMA instruction of kinds 5, 6, 7, 8
+MFMA_FLOP = {5: 2 * 32 * 32 * 16, 6: 2 * 32 * 32 * 64, 7: 2 * 32 * 32 * 64, 8: 2 * 32 * 32 * 16}
 
 
 def issue_cycles(kind: int, waves_per_simd: int):

@@ -89,8 +89,8 @@ def test_bf16_mfma_is_exact_and_the_f8f6f4_mfma_is_not(probes):
     a[:, 0] = big
     b[:, 0] = big
     exact = 448.0 * 448.0 + 63.0
-    d16 = probes.mfma_fp8(a, b, bf16_path=True)
-    d8 = probes.mfma_fp8(a, b, bf16_path=False)
+    d16 = probes.mfma_fp8(a, b, path="bf16")
+    d8 = probes.mfma_fp8(a, b, path="f8f6f4")
     assert np.all(d16 == exact)
     assert np.all(d8 != exact)
     # random operands with outlier channels: bf16 path within fp32 rounding of
@@ -104,8 +104,8 @@ def test_bf16_mfma_is_exact_and_the_f8f6f4_mfma_is_not(probes):
         ex = av @ bv.T
         big_prod = np.abs(av[:, None, :] * bv[None, :, :]).max(axis=2)
         absum = np.abs(av) @ np.abs(bv).T
-        d16 = probes.mfma_fp8(a, b, bf16_path=True)
-        d8 = probes.mfma_fp8(a, b, bf16_path=False)
+        d16 = probes.mfma_fp8(a, b, path="bf16")
+        d8 = probes.mfma_fp8(a, b, path="f8f6f4")
         worst16 = max(worst16, float((np.abs(d16 - ex) / absum).max()))
         worst8 = max(worst8, float((np.abs(d8 - ex) / big_prod).max()))
     print(f"[gpu] bf16 path: max |err| / sum|products| = {worst16:.2e}; "
