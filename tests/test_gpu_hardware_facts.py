@@ -8,10 +8,15 @@ checks: if one of them fails, the kernel that relies on it is wrong.
   fp8 tiles and the operand codes are computed with it.
 * v_cvt_scalef32_pk_fp4_f32 (scale 1) rounds to nearest even over the E2M1
   range and saturates at 6.
+* v_cvt_scalef32_pk_fp8_bf16 and v_cvt_scalef32_pk_fp4_bf16 give the codes
+  of x / scale, rounded to nearest even, for every bf16 value x and the
+  power-of-two scales the preparation kernel passes (2^-100 and up): it
+  converts the operands with them, straight from the packed bf16 words.
 * bf16 MFMAs over exactly widened E4M3 values give the fp32 sum of exact
   products, while one scaled f8f6f4 MFMA over the same codes does not: it
-  keeps only a limited number of bits below the largest product. This is why
-  the fp8 tiles' QK^T, whose rounding decides P codes, runs on bf16 MFMAs.
+  keeps only a limited number of bits below the largest product. Neither do
+  the unscaled 32x32x16 fp8 MFMAs, which also issue at the bf16 rate. This is
+  why the fp8 tiles' QK^T, whose rounding decides P codes, runs on bf16 MFMAs.
 """
 
 import numpy as np
@@ -71,6 +76,24 @@ def test_fp32_to_e2m1_rounds_to_nearest_even_and_saturates(probes):
     assert np.array_equal(probes.to_fp4(above), np.array([7, 7, 7, 15, 15], dtype=np.uint8))
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_bf16_scaled_conversion_divides_by_the_scale(probes, fmt):
+    lim, enc = (448.0, F.encode_e4m3) if fmt == "fp8" else (6.0, F.encode_e2m1)
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32).astype(np.float64)
+    finite = np.isfinite(vals)
+    for e in (-100, -20, -3, 0, 3, 20, 100):
+        sc = 2.0 ** e
+        y = np.where(finite, vals, 0.0) / sc
+        keep = finite & (np.abs(y) <= lim)
+        xb = bits[keep].astype(np.uint16)
+        if xb.size % 2:
+            xb = xb[:-1]
+        got = probes.bf16_to(xb, sc, fmt)
+        want = enc((xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64) / sc)
+        assert np.array_equal(got, want), f"{fmt} scale 2^{e}: {int((got != want).sum())} of {xb.size} codes differ"
+
+
 def _outlier_codes(rng, scale_idx):
     """E4M3 code matrices [32][64] of N(0,1)-like values, with two outlier
     channels (k indices) scaled x8, like the Small workload."""
@@ -91,12 +114,14 @@ def test_bf16_mfma_is_exact_and_the_f8f6f4_mfma_is_not(probes):
     exact = 448.0 * 448.0 + 63.0
     d16 = probes.mfma_fp8(a, b, path="bf16")
     d8 = probes.mfma_fp8(a, b, path="f8f6f4")
+    d8k16 = probes.mfma_fp8(a, b, path="fp8_k16")
     assert np.all(d16 == exact)
     assert np.all(d8 != exact)
+    assert np.all(d8k16 != exact)
     # random operands with outlier channels: bf16 path within fp32 rounding of
     # the exact sum; the f8f6f4 path's error relative to the largest product
     rng = np.random.default_rng(2)
-    worst16 = worst8 = 0.0
+    worst16 = worst8 = worst8k16 = 0.0
     for t in range(8):
         idx = rng.choice(64, 2, replace=False)
         a, b = _outlier_codes(rng, idx), _outlier_codes(rng, idx)
@@ -106,9 +131,13 @@ def test_bf16_mfma_is_exact_and_the_f8f6f4_mfma_is_not(probes):
         absum = np.abs(av) @ np.abs(bv).T
         d16 = probes.mfma_fp8(a, b, path="bf16")
         d8 = probes.mfma_fp8(a, b, path="f8f6f4")
+        d8k16 = probes.mfma_fp8(a, b, path="fp8_k16")
         worst16 = max(worst16, float((np.abs(d16 - ex) / absum).max()))
         worst8 = max(worst8, float((np.abs(d8 - ex) / big_prod).max()))
+        worst8k16 = max(worst8k16, float((np.abs(d8k16 - ex) / big_prod).max()))
     print(f"[gpu] bf16 path: max |err| / sum|products| = {worst16:.2e}; "
-          f"f8f6f4 path: max |err| / largest product = {worst8:.2e} (2^{np.log2(max(worst8, 1e-300)):.1f})")
+          f"f8f6f4 path: max |err| / largest product = {worst8:.2e} (2^{np.log2(max(worst8, 1e-300)):.1f}); "
+          f"fp8 32x32x16 path: {worst8k16:.2e} (2^{np.log2(max(worst8k16, 1e-300)):.1f})")
     assert worst16 <= 64 * 2.0 ** -24
     assert worst8 > 64 * 2.0 ** -24
+    assert worst8k16 > 64 * 2.0 ** -24
