@@ -264,7 +264,45 @@ __global__ __launch_bounds__(256) void k_mem(const uint4* __restrict__ src, floa
 
 }  // namespace
 
+// ---- LDS read rate: waves of one workgroup per CU streaming ds_read_b128 ----
+// Each wave reads 1 KiB per instruction (lane l: 16 bytes at 16 l of a
+// rotating window of a 64 KiB buffer, so no bank conflicts), kLdsIters x 16
+// reads, sixteen independent per trip. cyc[wave] = shader clocks for the
+// whole stream.
+constexpr int kLdsIters = 1024;
+
+__global__ __launch_bounds__(1024) void k_lds_read(float* sink, long long* cyc) {
+    extern __shared__ __align__(16) uint8_t lds[];   // 64 KiB used (96 KiB allocated: one workgroup per CU)
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < 65536 / 16; i += blockDim.x) reinterpret_cast<uint4*>(lds)[i] = make_uint4(i, 3 * i, 5 * i, 7 * i);
+    __syncthreads();
+    uint4 acc = {0, 0, 0, 0};
+    const int base = (w * 1024 + lane * 16) & 65535;
+    const long long t0 = clock64();
+    for (int it = 0; it < kLdsIters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint4 x = *reinterpret_cast<const uint4*>(lds + ((base + j * 4096 + it * 16) & 65520));
+            acc.x ^= x.x;
+            acc.y ^= x.y;
+            acc.z ^= x.z;
+            acc.w ^= x.w;
+        }
+    }
+    const long long t1 = clock64();
+    sink[blockIdx.x * blockDim.x + tid] = (float)(acc.x ^ acc.y ^ acc.z ^ acc.w);
+    if (lane == 0) cyc[blockIdx.x * 16 + w] = t1 - t0;
+}
+
 extern "C" {
+
+// waves: 4, 8 or 16 per workgroup (one workgroup on each of 256 CUs).
+// sink: device float[256 * 1024]; cyc: device int64[256 * 16] (per wave).
+int da2p_lds_read(int waves, float* sink, long long* cyc) {
+    if (waves != 4 && waves != 8 && waves != 16) return -1;
+    hipLaunchKernelGGL(k_lds_read, dim3(256), dim3(64 * waves), 96 * 1024, 0, sink, cyc);
+    return (int)hipDeviceSynchronize();
+}
 
 // mode 0..6 as above. src: device uint4[256 * 4 * 512 + 64]; out: device
 // float[256 * 256]; cyc: device int64[256 * 4]. cyc holds clocks for 512

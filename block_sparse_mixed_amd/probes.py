@@ -38,6 +38,7 @@ def lib():
         _lib.da2p_bf16_to.argtypes = [P, ctypes.c_float, P, ctypes.c_int, ctypes.c_int]
         _lib.da2p_issue.argtypes = [ctypes.c_int, ctypes.c_int, P, P]
         _lib.da2p_mem_issue.argtypes = [ctypes.c_int, P, P, P]
+        _lib.da2p_lds_read.argtypes = [ctypes.c_int, P, P]
     return _lib
 
 
@@ -139,6 +140,25 @@ def mem_issue_cycles(mode: int) -> float:
     return float(cyc.cpu().numpy().mean()) / (512 * 8)
 
 
+def lds_read_rate(waves: int):
+    """(clocks per ds_read_b128 per wave, bytes per clock per CU, wall TB/s
+    over the chip) for one workgroup of `waves` waves per CU streaming reads
+    from LDS."""
+    import time
+
+    import torch
+    sink = torch.empty(256 * 1024, dtype=torch.float32, device="cuda")
+    cyc = torch.zeros(256 * 16, dtype=torch.int64, device="cuda")
+    _ok(lib().da2p_lds_read(waves, sink.data_ptr(), cyc.data_ptr()), "lds_read")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _ok(lib().da2p_lds_read(waves, sink.data_ptr(), cyc.data_ptr()), "lds_read")   # synchronises
+    wall = time.perf_counter() - t0
+    c = float(cyc.view(256, 16)[:, :waves].float().mean())
+    reads = 1024 * 16
+    return c / reads, waves * reads * 1024 / c, 256 * waves * reads * 1024 / wall / 1e12
+
+
 def main():
     import torch
     print(f"device: {torch.cuda.get_device_name(0)}")
@@ -159,6 +179,12 @@ def main():
     print("|---|---|")
     for mode, name in MEM_MODES.items():
         print(f"| {name} | {mem_issue_cycles(mode):.1f} |")
+    print("\nLDS reads (ds_read_b128, 1 KiB per instruction), one workgroup per CU:")
+    print("\n| waves per CU | clocks per read per wave | bytes per clock per CU | TB/s over 256 CUs (wall) |")
+    print("|---|---|---|---|")
+    for waves in (4, 8, 16):
+        per, bpc, tbs = lds_read_rate(waves)
+        print(f"| {waves} | {per:.1f} | {bpc:.0f} | {tbs:.0f} |")
 
 if __name__ == "__main__":
     main()
