@@ -477,26 +477,31 @@ def time_layout(w, qd, kd, vd, pack, steps, warmup):
 def all_configs(args):
     """Every workload at its own budgets: step, preparation and attention
     times, throughput, roofline fraction and error vs dense fp32 (bf16
-    output, the production path)."""
+    output, the production path), and the oracle timed on the host over one
+    head in full (unless --no-cpu-baseline)."""
     import torch
 
     import synthetic as S
     for name in ("tiny", "small", "wan480p", "hunyuan720p"):
         w = S.WORKLOADS[name]
-        q, k, v = (t.to("cuda:0") for t in S.make_qkv(w))
+        qc, kc, vc = S.make_qkv(w)
+        q, k, v = (t.to("cuda:0") for t in (qc, kc, vc))
         info, prep_ms, attn_ms, step_ms, wall, out = time_layout(w, q, k, v, False, args.steps, args.warmup)
         dense, f_hi, f_lo = flops(w, info.n_blocks, info.n_hi, info.n_lo)
         t_star = f_hi / P_FP8 + f_lo / P_FP4
         att_s = sum(attn_ms) / len(attn_ms) / 1e3
         step_s = sum(step_ms) / len(step_ms) / 1e3
         err = dense_error(q, k, v, out, info.tau, args.error_rows)
+        cpu = None
+        if not args.no_cpu_baseline:
+            cpu = cpu_baseline(w, qc, kc, vc, 1, args.cpu_workers or default_workers())
         print(json.dumps({"workload": name, "n_blocks": info.n_blocks, "n_hi": info.n_hi, "n_lo": info.n_lo,
                           "attention_ms": att_s * 1e3, "attention_ms_min": min(attn_ms),
                           "prepare_ms": sum(prep_ms) / len(prep_ms), "step_ms_events": step_s * 1e3,
                           "dense_equiv_tflops_step": dense / step_s / 1e12,
                           "attention_executed_tflops": (f_hi + f_lo) / att_s / 1e12,
                           "blended_roofline_frac": t_star / att_s,
-                          "error_vs_dense_fp32": err}), flush=True)
+                          "error_vs_dense_fp32": err, "cpu_baseline": cpu}), flush=True)
         del q, k, v, out
         torch.cuda.empty_cache()
 

@@ -57,8 +57,9 @@
 //   loop body, values derived from the lane index recomputed where used,
 //   E2M1 operands kept as four dwords, and the rare rescale done in place.
 //
-//   The fp8 tiles' QK^T runs on bf16 MFMAs because the f8f6f4 MFMAs keep only
-//   about 12 bits below their largest product when they sum fp8 products:
+//   The fp8 tiles' QK^T runs on bf16 MFMAs because the f8f6f4 MFMAs (and the
+//   unscaled fp8 ones) keep only about 12 bits below their largest product
+//   when they sum fp8 products (tests/test_gpu_hardware_facts.py measures it):
 //   with outlier channels the scores move by ~1e-2 (log2 units), enough to
 //   flip the rounding of many P codes. Their PV product stays fp8: nothing is
 //   decided from its rounding.

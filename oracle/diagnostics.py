@@ -3,14 +3,13 @@
 TEST INFRASTRUCTURE ONLY, like the rest of this package: these functions
 measure the method on small inputs; nothing on the product path calls them.
 
-[DA2] "DraftAttention2" (arXiv 2609.32628), abstract: the output error of
-the method splits into a sparsification part (the interactions of skipped
-blocks are dropped) and an attention-weighted quantization part (retained
-blocks are computed in low precision); recovering skipped interactions with
-low-bit computation tightens the error bound when the quantization error it
-adds is smaller than the sparsification error it removes, which is why the
-method retains many blocks at low precision and keeps high precision for the
-blocks that carry the most attention mass.
+[DA2] "DraftAttention2" (arXiv 2609.32628), abstract: two terms make up the
+method's output error, one from the blocks it drops (sparsification) and one
+from the blocks it keeps at reduced precision, weighted by their attention
+(quantization). Moving a block from "skipped" to "4-bit" trades the first
+for the second, so it pays off whenever the block's rounding error is the
+smaller of the two; hence many blocks kept at low precision and the highest
+precision reserved for the blocks with the most attention mass.
 [DA1-article] (the news write-up of DraftAttention), theory paragraph: the
 draft map built from pooled queries and keys stays close to the full-
 resolution map in Frobenius norm, closer for spatially smooth latents, and
