@@ -261,8 +261,8 @@ __device__ __forceinline__ void v_row(const Tile& t, uint8_t* slot, int wr, cons
 template <int PH>
 __device__ __forceinline__ void k_extras(const Tile& t, uint8_t* slot, int w, int lane) {
     if constexpr (PH == kLo)
-        if (w == 1 && lane < 32) dma16(t.ks + lane * 16, slot + kKScale);
-    if (w == 0 && lane < 32) dma16(reinterpret_cast<const uint8_t*>(t.bias) + lane * 16, slot + kKBias);
+        if (w == 1 && lane < 32) dma16(t.ks + (uint32_t)lane * 16, slot + kKScale);
+    if (w == 0 && lane < 32) dma16(reinterpret_cast<const uint8_t*>(t.bias) + (uint32_t)lane * 16, slot + kKBias);
 }
 
 template <int PH, int I>
@@ -277,7 +277,7 @@ __device__ __forceinline__ void fetch_item(const Tile& tk, uint8_t* kslot, const
         k_extras<PH>(tk, kslot, w, lane);
     } else {
         static_assert(PH == kLo && I == 2 * kRows + 1, "fetch item");
-        if (w == 3 && lane < 32) dma16(tv.vs + lane * 16, vslot + kVScale);   // MXFP4 V scales
+        if (w == 3 && lane < 32) dma16(tv.vs + (uint32_t)lane * 16, vslot + kVScale);   // MXFP4 V scales
     }
 }
 
@@ -530,7 +530,7 @@ __device__ __forceinline__ void softmax(WaveState& st, const v16f (&s)[4], int e
     const float cs = PH == kHi ? fmaxf(ldexpf(st.c_lo, st.e_q + e_k), __FLT_MIN__) : st.c_lo;
     float gmax[2];                                       // per PV MFMA n: the lane's 32 raw scores
     block_max(s, gmax);
-    const float mnew = fmaxf(st.m, ceilf(cross2max(vmax(gmax[0], gmax[1])) * cs));
+    const float mnew = vmax(st.m, ceilf(cross2max(vmax(gmax[0], gmax[1])) * cs));
     if (!(st.mref >= mnew - kMaxLead)) {
         const float f = exp2f(st.mref - mnew);           // 0 while mref = -inf
 #pragma unroll
@@ -544,7 +544,7 @@ __device__ __forceinline__ void softmax(WaveState& st, const v16f (&s)[4], int e
         if constexpr (PH == kHi) {
             // finite also while no key has been seen (mnew = -inf): the
             // scores are then -inf and the codes 0
-            const float off = 8.0f - fmaxf(mnew, -__FLT_MAX__);
+            const float off = 8.0f - vmax(mnew, -__FLT_MAX__);
             static_for<8>([&](auto dc) __attribute__((always_inline)) {
                 constexpr int d = decltype(dc)::value;   // bytes 4 d .. 4 d + 3
                 const v16f& x = s[2 * n + (d >> 2)];
@@ -555,7 +555,7 @@ __device__ __forceinline__ void softmax(WaveState& st, const v16f (&s)[4], int e
                                             __builtin_amdgcn_exp2f(__builtin_fmaf(x[j + 3], cs, off)));
             });
             // 127 .. 127 + kMaxLead (127 while no key has been seen: both -inf)
-            psc[n] = 127 + (int)fmaxf(mnew - st.mref, 0.0f);
+            psc[n] = 127 + (int)vmax(mnew - st.mref, 0.0f);
         } else {
             // MX group of P = the lane's 32 keys of this PV MFMA: scale 2^F,
             // F the smallest integer with 2^(gmax cs) <= 6 * 2^F; codes
@@ -603,14 +603,16 @@ __device__ __forceinline__ void load_v(const uint8_t* vs, int n, int cb, int q, 
     // channel 32 cb + q; its swizzle depends on q only
     if constexpr (PH == kHi) {
         const int sw = swz_v8(q);
-        const uint8_t* row = vs + (32 * cb + q) * 128;
+        const uint8_t* row = vs + q * 128 + 4096 * cb;     // cb in the immediate offsets
         const uint4 x = *reinterpret_cast<const uint4*>(row + (((4 * n + h) ^ sw) << 4));
         const uint4 y = *reinterpret_cast<const uint4*>(row + (((4 * n + 2 + h) ^ sw) << 4));
         o.v = (v8i){(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
     } else {
-        const uint8_t* row = vs + (32 * cb + q) * 64;
+        // lane part + compile-time part, so that cb and n land in the
+        // instructions' immediate offsets
+        const uint8_t* row = vs + q * 64 + 2048 * cb;
         o.v = as_v4i(*reinterpret_cast<const uint4*>(row + (((2 * n + h) ^ swz_v4(q)) << 4)));
-        o.sc = vs[kVScale + (32 * cb + q) * 4 + 2 * n + h];
+        o.sc = vs[kVScale + q * 4 + h + 128 * cb + 2 * n];
     }
 }
 
