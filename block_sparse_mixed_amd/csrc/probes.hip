@@ -128,12 +128,16 @@ __global__ void k_bf16_to(const uint32_t* in, float scale, uint8_t* out, int pai
 
 // ---- issue costs with one or two waves per SIMD ----
 // cyc[wave] = shader clocks for kIters iterations of a block of kN
-// instructions of one kind (independent chains), per wave.
+// instructions of one kind (independent chains), per wave. Kinds 11 and 12
+// pair each exponential (11) or E2M1 pack conversion (12) with an independent
+// FMA of another chain; kind 13 runs exponentials in waves 0-3 and FMAs in
+// waves 4-7, so that with two waves per SIMD each SIMD holds one of each.
 constexpr int kIters = 2048;
 constexpr int kN = 16;
 
 template <int KIND>
-__device__ __forceinline__ void block(float (&f)[8], int (&iv)[8], v16f (&acc)[4], const v8i& oa, const v8bf& ob) {
+__device__ __forceinline__ void block(float (&f)[8], float (&g)[8], int (&iv)[8], v16f (&acc)[4], const v8i& oa,
+                                      const v8bf& ob) {
 #pragma unroll
     for (int t = 0; t < kN; ++t) {
         const int c = t & 7;
@@ -164,16 +168,25 @@ __device__ __forceinline__ void block(float (&f)[8], int (&iv)[8], v16f (&acc)[4
         if constexpr (KIND == 10)
             iv[c] = (int)__builtin_amdgcn_cvt_scalef32_pk_fp4_bf16((uint32_t)iv[c], __builtin_bit_cast(v2bf, iv[(c + 1) & 7]),
                                                                    f[c], 0);
+        if constexpr (KIND == 11) {
+            f[c] = __builtin_amdgcn_exp2f(f[c]);
+            g[c] = __builtin_fmaf(g[c], 1.0001f, 0.5f);
+        }
+        if constexpr (KIND == 12) {
+            iv[c] = (int)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32((uint32_t)iv[c], f[c], f[(c + 1) & 7], 1.0f, 0);
+            g[c] = __builtin_fmaf(g[c], 1.0001f, 0.5f);
+        }
     }
 }
 
 template <int KIND>
 __global__ __launch_bounds__(512) void k_issue(float* sink, long long* cyc) {
     const int lane = threadIdx.x & 63;
-    float f[8];
+    float f[8], g[8];
     int iv[8];
     for (int i = 0; i < 8; ++i) {
         f[i] = 0.01f * (lane + i);
+        g[i] = 0.02f * (lane - i);
         iv[i] = lane * 7 + i;
     }
     v16f acc[4] = {};
@@ -185,10 +198,17 @@ __global__ __launch_bounds__(512) void k_issue(float* sink, long long* cyc) {
     }
     __syncthreads();
     const long long t0 = clock64();
-    for (int it = 0; it < kIters; ++it) block<KIND>(f, iv, acc, oa, ob);
+    if constexpr (KIND == 13) {
+        if (threadIdx.x < 256)
+            for (int it = 0; it < kIters; ++it) block<1>(f, g, iv, acc, oa, ob);
+        else
+            for (int it = 0; it < kIters; ++it) block<0>(f, g, iv, acc, oa, ob);
+    } else {
+        for (int it = 0; it < kIters; ++it) block<KIND>(f, g, iv, acc, oa, ob);
+    }
     const long long t1 = clock64();
     float s = acc[0][0] + acc[1][1] + acc[2][2] + acc[3][3];
-    for (int i = 0; i < 8; ++i) s += f[i] + (float)iv[i];
+    for (int i = 0; i < 8; ++i) s += f[i] + g[i] + (float)iv[i];
     sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
     if (lane == 0) cyc[blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = t1 - t0;
 }
@@ -371,11 +391,15 @@ int da2p_bf16_to(const uint16_t* in, float scale, uint8_t* out, int n, int fmt) 
 // kind: 0 v_fma_f32, 1 v_exp_f32, 2 v_cvt_pk_fp8_f32, 3 v_cvt_scalef32_pk_fp4_f32,
 // 4 v_cvt_scalef32_pk_bf16_fp8, 5 mfma bf16 32x32x16, 6 mfma scaled fp8 32x32x64,
 // 7 mfma scaled fp4 32x32x64, 8 mfma fp8 32x32x16 (unscaled), 9
-// v_cvt_scalef32_pk_fp8_bf16, 10 v_cvt_scalef32_pk_fp4_bf16; waves_per_simd 1 or 2.
-// sink: device float[256 * 512]; cyc: device int64[256 * 8] (per wave).
-// Returns the HIP error; cyc holds clocks for 2048 x 16 instructions per wave.
+// v_cvt_scalef32_pk_fp8_bf16, 10 v_cvt_scalef32_pk_fp4_bf16, 11 v_exp_f32 paired
+// with an independent v_fma_f32, 12 v_cvt_scalef32_pk_fp4_f32 paired with one,
+// 13 v_exp_f32 waves beside v_fma_f32 waves (two waves per SIMD only);
+// waves_per_simd 1 or 2. sink: device float[256 * 512]; cyc: device
+// int64[256 * 8] (per wave). Returns the HIP error; cyc holds clocks for
+// 2048 x 16 steps per wave (a step of kinds 11 and 12 is two instructions).
 int da2p_issue(int kind, int waves_per_simd, float* sink, long long* cyc) {
     if (waves_per_simd != 1 && waves_per_simd != 2) return -1;
+    if (kind == 13 && waves_per_simd != 2) return -1;
     switch (kind) {
         case 0: return (int)run_issue(k_issue<0>, waves_per_simd, sink, cyc);
         case 1: return (int)run_issue(k_issue<1>, waves_per_simd, sink, cyc);
@@ -388,6 +412,9 @@ int da2p_issue(int kind, int waves_per_simd, float* sink, long long* cyc) {
         case 8: return (int)run_issue(k_issue<8>, waves_per_simd, sink, cyc);
         case 9: return (int)run_issue(k_issue<9>, waves_per_simd, sink, cyc);
         case 10: return (int)run_issue(k_issue<10>, waves_per_simd, sink, cyc);
+        case 11: return (int)run_issue(k_issue<11>, waves_per_simd, sink, cyc);
+        case 12: return (int)run_issue(k_issue<12>, waves_per_simd, sink, cyc);
+        case 13: return (int)run_issue(k_issue<13>, waves_per_simd, sink, cyc);
         default: return -1;
     }
 }

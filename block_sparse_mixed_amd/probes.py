@@ -106,10 +106,7 @@ def mfma_fp8(a_codes: np.ndarray, b_codes: np.ndarray, path: str) -> np.ndarray:
 MFMA_FLOP = {5: 2 * 32 * 32 * 16, 6: 2 * 32 * 32 * 64, 7: 2 * 32 * 32 * 64, 8: 2 * 32 * 32 * 16}
 
 
-def issue_cycles(kind: int, waves_per_simd: int):
-    """(clock-counter ticks per instruction of one kind per wave, averaged over
-    the launch; wall seconds of the launch) for one workgroup per CU and 1 or
-    2 waves per SIMD (256 workgroups)."""
+def _issue_raw(kind: int, waves_per_simd: int):
     import time
 
     import torch
@@ -120,8 +117,34 @@ def issue_cycles(kind: int, waves_per_simd: int):
     t0 = time.perf_counter()
     _ok(lib().da2p_issue(kind, waves_per_simd, sink.data_ptr(), cyc.data_ptr()), "issue")   # synchronises
     wall = time.perf_counter() - t0
-    c = cyc.cpu().numpy()[: 256 * 4 * waves_per_simd]
+    return cyc.cpu().numpy()[: 256 * 4 * waves_per_simd].reshape(256, 4 * waves_per_simd), wall
+
+
+def issue_cycles(kind: int, waves_per_simd: int):
+    """(clock-counter ticks per instruction of one kind per wave, averaged over
+    the launch; wall seconds of the launch) for one workgroup per CU and 1 or
+    2 waves per SIMD (256 workgroups)."""
+    c, wall = _issue_raw(kind, waves_per_simd)
     return float(c.mean()) / (ITERS * PER_ITER), wall
+
+
+def overlap():
+    """Whether an exponential or an E2M1 pack conversion shares issue time with
+    independent FMAs: ticks per step of an exponential (pack conversion) paired
+    with an FMA in one wave per SIMD, beside the ticks of each alone; and, with
+    two waves per SIMD, one issuing exponentials and the other FMAs, each
+    wave's ticks per instruction and the launch's wall time beside the
+    two-wave launches of either kind alone."""
+    step = ITERS * PER_ITER
+    t_fma, w_fma2 = issue_cycles(0, 1)[0], issue_cycles(0, 2)[1]
+    t_exp, w_exp2 = issue_cycles(1, 1)[0], issue_cycles(1, 2)[1]
+    t_cvt = issue_cycles(3, 1)[0]
+    t11 = issue_cycles(11, 1)[0]
+    t12 = issue_cycles(12, 1)[0]
+    c13, w13 = _issue_raw(13, 2)
+    return {"fma": t_fma, "exp": t_exp, "cvt_pk_fp4": t_cvt, "exp+fma": t11, "cvt_pk_fp4+fma": t12,
+            "mixed_exp_wave": float(c13[:, :4].mean()) / step, "mixed_fma_wave": float(c13[:, 4:].mean()) / step,
+            "mixed_wall": w13, "exp2_wall": w_exp2, "fma2_wall": w_fma2}
 
 
 MEM_MODES = {0: "16 FMAs only", 1: "global_load_dwordx4 + 16 FMAs", 2: "global_load_lds_dwordx4 + 16 FMAs",
@@ -173,6 +196,17 @@ def main():
         n1 = 256 * 4 * ITERS * PER_ITER
         tf = f"{n1 * MFMA_FLOP[k] / w1 / 1e12:.0f} / {2 * n1 * MFMA_FLOP[k] / w2 / 1e12:.0f}" if k in MFMA_FLOP else ""
         print(f"| {name} | {t1:.1f} | {t1 * w2 / (2 * w1):.1f} | {tf} |")
+    o = overlap()
+    print("\noverlap of exponentials and pack conversions with independent FMAs (ticks per step):")
+    print("\n| stream | ticks | the two alone, summed |")
+    print("|---|---|---|")
+    print(f"| v_exp_f32 + v_fma_f32, one wave per SIMD | {o['exp+fma']:.1f} | {o['exp'] + o['fma']:.1f} |")
+    print(f"| v_cvt_scalef32_pk_fp4_f32 + v_fma_f32, one wave per SIMD | {o['cvt_pk_fp4+fma']:.1f} | "
+          f"{o['cvt_pk_fp4'] + o['fma']:.1f} |")
+    print(f"\ntwo waves per SIMD, one of exponentials and one of FMAs: exponential wave "
+          f"{o['mixed_exp_wave']:.1f} ticks per instruction, FMA wave {o['mixed_fma_wave']:.1f}; wall "
+          f"{o['mixed_wall'] * 1e3:.2f} ms against {o['exp2_wall'] * 1e3:.2f} ms (two exponential waves) and "
+          f"{o['fma2_wall'] * 1e3:.2f} ms (two FMA waves)")
     print("\nmemory instructions among independent FMAs, one wave per SIMD (ticks per memory instruction")
     print("and its 16 FMAs; the difference to the FMA-only row is the memory instruction's issue cost):")
     print("\n| stream | ticks |")
