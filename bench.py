@@ -83,6 +83,9 @@ def parse():
                     help="packed edge windows (partial windows streamed into shared blocks) for the timed line and the sweep")
     ap.add_argument("--no-alt-layout", action="store_true",
                     help="do not also time the other block layout")
+    ap.add_argument("--budgets", type=float, nargs=2, metavar=("HI", "LO"),
+                    help="override the workload's hi and lo budgets (fractions of key blocks) for the timed line; "
+                         "the workload is then named with them, and its traffic figure is not reported")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a streaming kernel of known size (read 1 GiB, write 1 GiB), for counter scaling")
     return ap.parse_args()
@@ -602,6 +605,8 @@ def main():
 
     w = S.WORKLOADS[args.workload]
     q, k, v = S.make_qkv(w)
+    if args.budgets:
+        w = S.with_budgets(w, *args.budgets)
     if args.pack_edges:
         w = dataclasses.replace(w, name=w.name + "-packed", pack_edges=True)
     cpu = None
