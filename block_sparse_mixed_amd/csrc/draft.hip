@@ -14,11 +14,12 @@
 // which either adjacent label is accepted.
 //
 //   draft_logits_kernel : L[m][bh][i][j] = tau * <P_m,q[i], P_m,k[j]>, m in {avg, max};
-//                         64x64 output tile per workgroup, 4x4 per thread.
-//   rank_kernel         : per (bh, query block i): row softmax of both maps,
-//                         C = (A_avg + A_max) / 2, bitonic sort on
-//                         (C descending, index ascending), labels, and the
-//                         hi/lo index lists in that rank order.
+//                         32x32 output tile per workgroup, fp64 MFMAs.
+//   rank_wave_kernel    : per (bh, query block i), one wave (rows of up to
+//   rank_kernel           1024 blocks) or one workgroup (larger rows): row
+//                         softmax of both maps, C = (A_avg + A_max) / 2,
+//                         bitonic sort on (C descending, index ascending),
+//                         labels, and the hi/lo index lists in that rank order.
 //   set_labels_kernel   : test hook; ascending lists from given labels by
 //                         ballot compaction, count check.
 #include "common.hpp"
@@ -27,73 +28,94 @@ namespace da2 {
 
 namespace {
 
-constexpr int kTile = 64;
-constexpr int kKc = 32;
+constexpr int kTile = 32;
 
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+// One workgroup: a 32 x 32 tile of one map's logits, as 2 x 2 fp64 MFMA
+// tiles (V_MFMA_F64_16X16X4_F64: lane l gives A row l % 16 and B column
+// l % 16 at k = l / 16, and gets D rows l / 16 + 4 e, e = 0 .. 3, of column
+// l % 16). The four waves split the channels, 32 each, so that every wave
+// issues all of its loads at once and the memory latency is paid once per
+// workgroup rather than once per channel chunk; their partial sums then add
+// up through LDS in a fixed order. Within a wave the channel order of the
+// contraction is free as long as both operands agree: lane group
+// g = l / 16 feeds channels 32 w + 8 g + s to the step-s MFMA, so that
+// every lane reads 64 contiguous bytes of each of its rows. The sums run in
+// fp64, each product and addition rounded once, as in a plain loop of fused
+// multiply-adds (in another order).
+// A one-dimensional grid of (map, head) slices times t x t tiles, in an
+// XCD-aware order: the workgroups one XCD receives (every eighth) take
+// consecutive tiles of the same slices, so that a slice's pooled rows are
+// fetched into one L2 rather than into all eight.
 __global__ __launch_bounds__(256) void draft_logits_kernel(Geo g, const double* __restrict__ pool,
                                                            double* __restrict__ logits) {
-    const int m = blockIdx.z & 1;           // 0 = avg map, 1 = max map
-    const int bh = blockIdx.z >> 1;
-    const int i0 = blockIdx.y * kTile;
-    const int j0 = blockIdx.x * kTile;
-    const int tid = threadIdx.x;
-    const int tx = tid & 15, ty = tid >> 4;
     const int nb = g.n_blocks;
+    const int t = (nb + kTile - 1) / kTile;
+    const int total = 2 * g.bh * t * t;
+    const int xcd = blockIdx.x & 7, k8 = blockIdx.x >> 3;
+    const int per = total >> 3, rem = total & 7;
+    const int logical = xcd * per + min(xcd, rem) + k8;
+    const int slice = logical / (t * t), tile = logical - slice * (t * t);
+    const int m = slice & 1;                // 0 = avg map, 1 = max map
+    const int bh = slice >> 1;
+    const int i0 = (tile / t) * kTile, j0 = (tile % t) * kTile;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const uint64_t plane = (uint64_t)g.bh * nb * DA2_DPAD;
     const double* qp = pool + (uint64_t)(m) * plane + (uint64_t)bh * nb * DA2_DPAD;       // q avg / q max
     const double* kp = pool + (uint64_t)(2 + m) * plane + (uint64_t)bh * nb * DA2_DPAD;   // k avg / k max
+    const int r = lane & 15, kg = lane >> 4;
+    const int c0 = 32 * w + 8 * kg;         // this lane's first channel
+    const bool chan = 32 * w < g.head_dim;  // the wave has channels to sum
 
-    // channel-major staging: thread (tx, ty) reads rows 4 ty .. 4 ty + 3 of
-    // Q and 4 tx .. 4 tx + 3 of K as two 16-byte reads each
-    __shared__ __align__(16) double qs[kKc][kTile + 2];
-    __shared__ __align__(16) double ks[kKc][kTile + 2];
-    // the next channel chunk is read into registers while this one is used
-    constexpr int kPer = kTile * kKc / 256;
-    double qn[kPer], kn[kPer];
-    auto gload = [&](int c0) __attribute__((always_inline)) {
+    v4d acc[2][2];
 #pragma unroll
-        for (int t = 0; t < kPer; ++t) {
-            const int e = tid + 256 * t;
-            const int r = e / kKc, cc = e % kKc;
-            qn[t] = (i0 + r < nb) ? qp[(uint64_t)(i0 + r) * DA2_DPAD + c0 + cc] : 0.0;
-            kn[t] = (j0 + r < nb) ? kp[(uint64_t)(j0 + r) * DA2_DPAD + c0 + cc] : 0.0;
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = (v4d){0.0, 0.0, 0.0, 0.0};
+    if (chan) {
+        // A rows (queries) i0 + 16 tt + r, B rows (keys) j0 + 16 tt + r; a
+        // row past the end is read from row 0, unconditionally, and zeroed
+        double ca[2][8], cb[2][8];
+        auto load = [&](double (&x)[8], const double* base, int row) __attribute__((always_inline)) {
+            const bool ok = row < nb;
+            const double2* src = reinterpret_cast<const double2*>(base + (uint64_t)(ok ? row : 0) * DA2_DPAD + c0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const double2 v = src[u];
+                x[2 * u] = ok ? v.x : 0.0;
+                x[2 * u + 1] = ok ? v.y : 0.0;
+            }
+        };
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            load(ca[tt], qp, i0 + 16 * tt + r);
+            load(cb[tt], kp, j0 + 16 * tt + r);
         }
-    };
-    double acc[4][4] = {};
-    gload(0);
-    for (int c0 = 0; c0 < g.head_dim; c0 += kKc) {
 #pragma unroll
-        for (int t = 0; t < kPer; ++t) {
-            const int e = tid + 256 * t;
-            const int r = e / kKc, cc = e % kKc;
-            qs[cc][r] = qn[t];
-            ks[cc][r] = kn[t];
+        for (int s = 0; s < 8; ++s) {
+            acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(ca[0][s], cb[0][s], acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(ca[0][s], cb[1][s], acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(ca[1][s], cb[0][s], acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(ca[1][s], cb[1][s], acc[1][1], 0, 0, 0);
         }
-        __syncthreads();
-        if (c0 + kKc < g.head_dim) gload(c0 + kKc);
-#pragma unroll 4
-        for (int cc = 0; cc < kKc; ++cc) {
-            const double2 q01 = *reinterpret_cast<const double2*>(&qs[cc][4 * ty]);
-            const double2 q23 = *reinterpret_cast<const double2*>(&qs[cc][4 * ty + 2]);
-            const double2 k01 = *reinterpret_cast<const double2*>(&ks[cc][4 * tx]);
-            const double2 k23 = *reinterpret_cast<const double2*>(&ks[cc][4 * tx + 2]);
-            const double qa[4] = {q01.x, q01.y, q23.x, q23.y};
-            const double kb[4] = {k01.x, k01.y, k23.x, k23.y};
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int w = 0; w < 4; ++w) acc[u][w] = fma(qa[u], kb[w], acc[u][w]);
-        }
-        __syncthreads();
     }
+    // partial sums [wave][MFMA tile][element][lane], then each thread adds the
+    // four waves' values of four outputs in wave order
+    __shared__ double part[4][4][4][64];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part[w][k][e][lane] = acc[k >> 1][k & 1][e];
+    __syncthreads();
     double* out = logits + (uint64_t)m * g.bh * nb * nb + (uint64_t)bh * nb * nb;
+    const int e = w;                        // this thread's element index
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int i = i0 + 4 * ty + u, j = j0 + 4 * tx + w;
-            if (i < nb && j < nb) out[(uint64_t)i * nb + j] = g.tau * acc[u][w];
-        }
+    for (int k = 0; k < 4; ++k) {
+        const double v = ((part[0][k][e][lane] + part[1][k][e][lane]) + part[2][k][e][lane]) + part[3][k][e][lane];
+        const int i = i0 + 16 * (k >> 1) + kg + 4 * e, j = j0 + 16 * (k & 1) + r;
+        if (i < nb && j < nb) out[(uint64_t)i * nb + j] = g.tau * v;
+    }
 }
 
 // The value of lane l ^ D (D < 64, a power of two) without a trip through
@@ -185,8 +207,10 @@ __device__ __forceinline__ int compact_list(const int8_t* lab, int nb, int8_t wa
 }
 
 // "a before b" in rank order: larger C first, then the lower block index.
+// Bitwise operators, so that the three comparisons combine as lane masks
+// rather than as branches.
 __device__ __forceinline__ bool before(double va, int ia, double vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
+    return (va > vb) | ((va == vb) & (ia < ib));
 }
 
 // Bitonic sort of np = 256 R (value, index) pairs held in registers: lane l
@@ -282,14 +306,14 @@ __device__ __forceinline__ void bitonic_step(SortState<R>& st, double* val, int3
 
 // compile-time stages for the small sizes (every condition of a step folds
 // away); a plain loop for the large ones, whose full unrolling is too big
-template <int R, int K, int JJ>
+template <int R, int K, int JJ, int NP = 256 * R>
 __device__ __forceinline__ void bitonic_stages(SortState<R>& st, double* val, int32_t* idx, int base) {
-    if constexpr (K <= 256 * R) {
+    if constexpr (K <= NP) {
         bitonic_step<R, (JJ >= R && JJ < 64 * R) ? JJ / R : 0>(st, val, idx, base, K, JJ);
         if constexpr (JJ > 1)
-            bitonic_stages<R, K, JJ / 2>(st, val, idx, base);
+            bitonic_stages<R, K, JJ / 2, NP>(st, val, idx, base);
         else
-            bitonic_stages<R, 2 * K, K>(st, val, idx, base);
+            bitonic_stages<R, 2 * K, K, NP>(st, val, idx, base);
     }
 }
 
@@ -395,6 +419,86 @@ __global__ __launch_bounds__(256) void rank_kernel(Geo g, double* __restrict__ s
     }
 }
 
+// The same ranking with one wave per row, for rows of at most 1024 blocks
+// (np = 64 R): the row's values stay in the wave's registers from the loads
+// through the sort (lane l holds elements R l .. R l + R - 1), so no step
+// needs LDS or a barrier; only the labels pass through LDS, to be written
+// out in raster order. Four rows per workgroup.
+template <int R>
+__global__ __launch_bounds__(256) void rank_wave_kernel(Geo g, double* __restrict__ scores, int8_t* __restrict__ labels,
+                                                        int32_t* __restrict__ hi_list, int32_t* __restrict__ lo_list) {
+    constexpr int np = 64 * R;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int i = blockIdx.x * 4 + w;
+    const int bh = blockIdx.y;
+    const int nb = g.n_blocks;
+    __shared__ int8_t lab_all[4][np];
+    if (i >= nb) return;                 // no barriers below
+    int8_t* lab = lab_all[w];
+    double* row_avg = scores + ((uint64_t)bh * nb + i) * nb;
+    const double* row_max = scores + (uint64_t)g.bh * nb * nb + ((uint64_t)bh * nb + i) * nb;
+    const int base = R * lane;
+
+    // combined score C = (softmax(avg row) + softmax(max row)) / 2
+    double va[R], vm[R];
+    double mx = -__builtin_huge_val(), mx2 = -__builtin_huge_val();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int j = base + r;
+        va[r] = j < nb ? row_avg[j] : -__builtin_huge_val();
+        vm[r] = j < nb ? row_max[j] : -__builtin_huge_val();
+        mx = fmax(mx, va[r]);
+        mx2 = fmax(mx2, vm[r]);
+    }
+    butterfly_max2<32>(mx, mx2);
+    double sm = 0.0, sm2 = 0.0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        va[r] = base + r < nb ? exp(va[r] - mx) : 0.0;
+        vm[r] = base + r < nb ? exp(vm[r] - mx2) : 0.0;
+        sm += va[r];
+        sm2 += vm[r];
+    }
+    butterfly_sum2<32>(sm, sm2);
+    SortState<R> st;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int j = base + r;
+        st.ix[r] = j;
+        if (j < nb) {
+            st.v[r] = 0.5 * (va[r] / sm + vm[r] / sm2);
+            row_avg[j] = st.v[r];   // section 0 of the scores now holds C for this row
+        } else {
+            st.v[r] = -1.0;         // sorts after every real score (C >= 0)
+        }
+    }
+
+    // bitonic sort, "a before b" iff C_a > C_b or (C_a == C_b and index_a < index_b);
+    // every step's partner is in the lane or in the wave
+    bitonic_stages<R, 2, 1, np>(st, nullptr, nullptr, base);
+
+    const int n_ret = g.n_hi + g.n_lo;
+    const uint64_t rowid = (uint64_t)bh * nb + i;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int pos = base + r;      // rank of the element this lane now holds
+        if (pos < nb) lab[st.ix[r]] = (int8_t)(pos < g.n_hi ? DA2_HI : (pos < n_ret ? DA2_LO : DA2_SKIP));
+        // lists in rank order (best first)
+        if (pos < g.n_hi)
+            hi_list[rowid * g.n_hi + pos] = st.ix[r];
+        else if (pos < n_ret)
+            lo_list[rowid * g.n_lo + (pos - g.n_hi)] = st.ix[r];
+    }
+    // the wave's own LDS writes, read back by its other lanes: LDS
+    // instructions of one wave complete in order; the fence keeps the
+    // compiler from moving the reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int8_t* lrow = labels + rowid * nb;
+    for (int j = lane; j < nb; j += 64) lrow[j] = lab[j];
+}
+
 __global__ __launch_bounds__(64) void set_labels_kernel(Geo g, const int8_t* __restrict__ src, int8_t* __restrict__ labels,
                                                         int32_t* __restrict__ hi_list, int32_t* __restrict__ lo_list,
                                                         uint32_t* __restrict__ status) {
@@ -422,10 +526,22 @@ hipError_t launch_draft(const Geo& g, const Layout& L, void* ws, hipStream_t str
     const double* pool = reinterpret_cast<const double*>(base + L.pool);
     double* scores = reinterpret_cast<double*>(base + L.scores);
     const int t = (g.n_blocks + kTile - 1) / kTile;
-    hipError_t e = launch_kernel(draft_logits_kernel, dim3(t, t, 2 * g.bh), dim3(256), 0, stream, g, pool, scores);
+    hipError_t e = launch_kernel(draft_logits_kernel, dim3(2 * g.bh * t * t), dim3(256), 0, stream, g, pool, scores);
     if (e != hipSuccess) return e;
     int np = 256;
     while (np < g.n_blocks) np <<= 1;
+    if (np <= 1024) {
+        auto run_wave = [&](auto kernel) {
+            return launch_kernel(kernel, dim3((g.n_blocks + 3) / 4, g.bh), dim3(256), 0, stream, g, scores,
+                                 reinterpret_cast<int8_t*>(base + L.labels), reinterpret_cast<int32_t*>(base + L.hi),
+                                 reinterpret_cast<int32_t*>(base + L.lo));
+        };
+        switch (np) {
+            case 256: return run_wave(rank_wave_kernel<4>);
+            case 512: return run_wave(rank_wave_kernel<8>);
+            default: return run_wave(rank_wave_kernel<16>);
+        }
+    }
     const size_t shmem = (size_t)np * (8 + 8 + 4 + 1);
     auto run = [&](auto kernel) {
         return launch_kernel(kernel, dim3(g.n_blocks, g.bh), dim3(256), shmem, stream, g, scores,
@@ -433,9 +549,6 @@ hipError_t launch_draft(const Geo& g, const Layout& L, void* ws, hipStream_t str
                              reinterpret_cast<int32_t*>(base + L.lo));
     };
     switch (np >> 8) {
-        case 1: return run(rank_kernel<1>);
-        case 2: return run(rank_kernel<2>);
-        case 4: return run(rank_kernel<4>);
         case 8: return run(rank_kernel<8>);
         default: return run(rank_kernel<16>);      // np <= DA2_MAX_BLOCKS = 4096
     }

@@ -13,6 +13,9 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v8f __attribute__((ext_vector_type(8)));
+typedef double v4d __attribute__((ext_vector_type(4)));
+typedef double v8d __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
@@ -168,6 +171,16 @@ __device__ __forceinline__ void block(float (&f)[8], float (&g)[8], int (&iv)[8]
         if constexpr (KIND == 10)
             iv[c] = (int)__builtin_amdgcn_cvt_scalef32_pk_fp4_bf16((uint32_t)iv[c], __builtin_bit_cast(v2bf, iv[(c + 1) & 7]),
                                                                    f[c], 0);
+        if constexpr (KIND == 14) {
+            const v4d d = __builtin_amdgcn_mfma_f64_16x16x4f64((double)f[t & 7], (double)g[t & 7],
+                                                              __builtin_bit_cast(v4d, acc[t & 3].lo), 0, 0, 0);
+            acc[t & 3].lo = __builtin_bit_cast(v8f, d);
+        }
+        if constexpr (KIND == 15) {   // sixteen independent fp64 FMA chains in the accumulators
+            v8d x = __builtin_bit_cast(v8d, acc[t & 3]);
+            x[(t >> 2) & 7] = __builtin_fma(x[(t >> 2) & 7], 1.0000001, 0.5);
+            acc[t & 3] = __builtin_bit_cast(v16f, x);
+        }
         if constexpr (KIND == 11) {
             f[c] = __builtin_amdgcn_exp2f(f[c]);
             g[c] = __builtin_fmaf(g[c], 1.0001f, 0.5f);
@@ -393,7 +406,8 @@ int da2p_bf16_to(const uint16_t* in, float scale, uint8_t* out, int n, int fmt) 
 // 7 mfma scaled fp4 32x32x64, 8 mfma fp8 32x32x16 (unscaled), 9
 // v_cvt_scalef32_pk_fp8_bf16, 10 v_cvt_scalef32_pk_fp4_bf16, 11 v_exp_f32 paired
 // with an independent v_fma_f32, 12 v_cvt_scalef32_pk_fp4_f32 paired with one,
-// 13 v_exp_f32 waves beside v_fma_f32 waves (two waves per SIMD only);
+// 13 v_exp_f32 waves beside v_fma_f32 waves (two waves per SIMD only), 14
+// mfma f64 16x16x4, 15 v_fma_f64;
 // waves_per_simd 1 or 2. sink: device float[256 * 512]; cyc: device
 // int64[256 * 8] (per wave). Returns the HIP error; cyc holds clocks for
 // 2048 x 16 steps per wave (a step of kinds 11 and 12 is two instructions).
@@ -415,6 +429,8 @@ int da2p_issue(int kind, int waves_per_simd, float* sink, long long* cyc) {
         case 11: return (int)run_issue(k_issue<11>, waves_per_simd, sink, cyc);
         case 12: return (int)run_issue(k_issue<12>, waves_per_simd, sink, cyc);
         case 13: return (int)run_issue(k_issue<13>, waves_per_simd, sink, cyc);
+        case 14: return (int)run_issue(k_issue<14>, waves_per_simd, sink, cyc);
+        case 15: return (int)run_issue(k_issue<15>, waves_per_simd, sink, cyc);
         default: return -1;
     }
 }

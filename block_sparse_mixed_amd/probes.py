@@ -20,7 +20,7 @@ KINDS = {0: "v_fma_f32", 1: "v_exp_f32", 2: "v_cvt_pk_fp8_f32 (2 values)", 3: "v
          4: "v_cvt_scalef32_pk_bf16_fp8 (2 values)", 5: "v_mfma_f32_32x32x16_bf16",
          6: "v_mfma_scale_f32_32x32x64_f8f6f4 (fp8)", 7: "v_mfma_scale_f32_32x32x64_f8f6f4 (fp4)",
          8: "v_mfma_f32_32x32x16_fp8_fp8", 9: "v_cvt_scalef32_pk_fp8_bf16 (2 values)",
-         10: "v_cvt_scalef32_pk_fp4_bf16 (2 values)"}
+         10: "v_cvt_scalef32_pk_fp4_bf16 (2 values)", 14: "v_mfma_f64_16x16x4_f64", 15: "v_fma_f64"}
 ITERS, PER_ITER = 2048, 16
 
 
@@ -103,7 +103,8 @@ def mfma_fp8(a_codes: np.ndarray, b_codes: np.ndarray, path: str) -> np.ndarray:
 
 
 # flops per MFMA instruction of kinds 5, 6, 7, 8
-MFMA_FLOP = {5: 2 * 32 * 32 * 16, 6: 2 * 32 * 32 * 64, 7: 2 * 32 * 32 * 64, 8: 2 * 32 * 32 * 16}
+MFMA_FLOP = {5: 2 * 32 * 32 * 16, 6: 2 * 32 * 32 * 64, 7: 2 * 32 * 32 * 64, 8: 2 * 32 * 32 * 16, 14: 2 * 16 * 16 * 4,
+             15: 2 * 64}
 
 
 def _issue_raw(kind: int, waves_per_simd: int):
