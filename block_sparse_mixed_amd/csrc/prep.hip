@@ -40,6 +40,8 @@ struct PrepArgs {
 namespace {
 
 typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 typedef short v2s16 __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 
@@ -51,6 +53,27 @@ constexpr uint32_t kAbs2 = 0x7FFF7FFFu;   // magnitude bits of two packed bf16 v
 // hardware flushes it. Smaller exponents (blocks or groups of magnitude below
 // about 2^-92) multiply by 2^-e in fp32 first.
 constexpr int kMinScaledExp = -100;
+
+// Streaming accesses (the nt bit): the bf16 inputs are read once, and the
+// codes are read by the attention kernel only after the rest of the
+// preparation has moved some 600 MB through the caches, so neither gains
+// from staying in L2; marked non-temporal they leave it to the pooled values
+// and the tile tables (measured: back to back, the Q/K kernel 6 % and the V
+// kernel 12 % faster; in the step, after an attention launch, the whole
+// preparation 1.6 % faster, the attention unchanged).
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+    const v4u32 t = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void store_stream(void* p, uint4 v) {
+    __builtin_nontemporal_store((v4u32){v.x, v.y, v.z, v.w}, reinterpret_cast<v4u32*>(p));
+}
+__device__ __forceinline__ void store_stream(void* p, uint2 v) {
+    __builtin_nontemporal_store((v2u32){v.x, v.y}, reinterpret_cast<v2u32*>(p));
+}
+__device__ __forceinline__ void store_stream(void* p, uint32_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
 
 // Per-half unsigned maximum of two pairs of 16-bit values (V_PK_MAX_U16).
 __device__ __forceinline__ uint32_t max2_u16(uint32_t a, uint32_t b) {
@@ -206,7 +229,7 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrepArgs a, int per) 
         const int s = (tid >> 4) + 16 * it;
         const int64_t n = sr[s];
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (n >= 0 && chan_real) v = *reinterpret_cast<const uint4*>(src + n * g.stride_n + cc * 8);
+        if (n >= 0 && chan_real) v = load_stream(src + n * g.stride_n + cc * 8);
         realm |= (n >= 0 ? 1u : 0u) << it;
         c = v;
     };
@@ -307,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrepArgs a, int per) 
                 w8 = fp8x8_small(v, e8);
             else
                 w8 = fp8x8_scaled(v, exp2i(max(e8, kMinScaledExp)));
-            *reinterpret_cast<uint2*>(c8 + 16 * DA2_DPAD * it + o8) = w8;
+            store_stream(c8 + 16 * DA2_DPAD * it + o8, w8);
             // 32-channel group = 4 consecutive lanes (DPP quad permutations)
             uint32_t gm = cmax[it];
             gm = max2_u16(gm, (uint32_t)__builtin_amdgcn_mov_dpp((int)gm, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
@@ -319,7 +342,7 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrepArgs a, int per) 
                 w4 = fp4x8_small(v, e4);
             else
                 w4 = fp4x8_scaled(v, exp2i(max(e4, kMinScaledExp)));
-            *reinterpret_cast<uint32_t*>(c4 + 16 * (DA2_DPAD / 2) * it + o4) = w4;
+            store_stream(c4 + 16 * (DA2_DPAD / 2) * it + o4, w4);
             if ((cc & 3) == 0) s4[16 * (DA2_DPAD / 32) * it + os4] = (uint8_t)(e4 + 127);
             float x[8];
             unpack8(v, x);
@@ -421,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrepArgs a, int per) 
                             pack_fp8x4(col(j) * inv, col(j + 1) * inv, col(j + 2) * inv, col(j + 3) * inv);
                 } else {
                     const uint2 lo = fp8x8_scaled(pr[0], sc8), hi = fp8x8_scaled(pr[1], sc8);
-                    *reinterpret_cast<uint4*>(c8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    store_stream(c8, make_uint4(lo.x, lo.y, hi.x, hi.y));
                 }
                 const uint32_t gm = ch ? am >> 16 : am & 0xFFFFu;
                 const int e4 = fp4_exponent(bf16_bits_to_f32(gm));
@@ -436,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrepArgs a, int per) 
                     }
                 } else {
                     const float sc = exp2i(max(e4, kMinScaledExp));
-                    *reinterpret_cast<uint2*>(c4) = make_uint2(fp4x8_scaled(pr[0], sc), fp4x8_scaled(pr[1], sc));
+                    store_stream(c4, make_uint2(fp4x8_scaled(pr[0], sc), fp4x8_scaled(pr[1], sc)));
                 }
                 if ((sg & 1) == 0) *s4 = (uint8_t)(e4 + 127);
                 __builtin_amdgcn_sched_barrier(0);   // one channel at a time
