@@ -54,13 +54,13 @@ constexpr uint32_t kAbs2 = 0x7FFF7FFFu;   // magnitude bits of two packed bf16 v
 // about 2^-92) multiply by 2^-e in fp32 first.
 constexpr int kMinScaledExp = -100;
 
-// Streaming accesses (the nt bit): the bf16 inputs are read once, and the
-// codes are read by the attention kernel only after the rest of the
-// preparation has moved some 600 MB through the caches, so neither gains
-// from staying in L2; marked non-temporal they leave it to the pooled values
-// and the tile tables (measured: back to back, the Q/K kernel 6 % and the V
-// kernel 12 % faster; in the step, after an attention launch, the whole
-// preparation 1.6 % faster, the attention unchanged).
+// Streaming accesses (the nt bit) for the V kernel: its bf16 input is read
+// once, and its codes are read by the attention kernel only after some
+// hundreds of MB have passed through the caches, so neither gains from
+// staying in L2. Measured in the step (interleaved medians of the
+// preparation): 0.2006 ms with plain accesses, 0.1996 with streaming loads
+// and code stores in both kernels, 0.1967 with them in the V kernel only
+// (the Q/K kernel then ran slower after an attention launch).
 __device__ __forceinline__ uint4 load_stream(const void* p) {
     const v4u32 t = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(p));
     return make_uint4(t.x, t.y, t.z, t.w);
@@ -70,9 +70,6 @@ __device__ __forceinline__ void store_stream(void* p, uint4 v) {
 }
 __device__ __forceinline__ void store_stream(void* p, uint2 v) {
     __builtin_nontemporal_store((v2u32){v.x, v.y}, reinterpret_cast<v2u32*>(p));
-}
-__device__ __forceinline__ void store_stream(void* p, uint32_t v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
 }
 
 // Per-half unsigned maximum of two pairs of 16-bit values (V_PK_MAX_U16).
@@ -229,7 +226,8 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrepArgs a, int per) 
         const int s = (tid >> 4) + 16 * it;
         const int64_t n = sr[s];
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (n >= 0 && chan_real) v = load_stream(src + n * g.stride_n + cc * 8);
+        if (n >= 0 && chan_real) v = kV ? load_stream(src + n * g.stride_n + cc * 8)
+                                        : *reinterpret_cast<const uint4*>(src + n * g.stride_n + cc * 8);
         realm |= (n >= 0 ? 1u : 0u) << it;
         c = v;
     };
@@ -330,7 +328,7 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrepArgs a, int per) 
                 w8 = fp8x8_small(v, e8);
             else
                 w8 = fp8x8_scaled(v, exp2i(max(e8, kMinScaledExp)));
-            store_stream(c8 + 16 * DA2_DPAD * it + o8, w8);
+            *reinterpret_cast<uint2*>(c8 + 16 * DA2_DPAD * it + o8) = w8;
             // 32-channel group = 4 consecutive lanes (DPP quad permutations)
             uint32_t gm = cmax[it];
             gm = max2_u16(gm, (uint32_t)__builtin_amdgcn_mov_dpp((int)gm, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
@@ -342,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 4) void prep_kernel(PrepArgs a, int per) 
                 w4 = fp4x8_small(v, e4);
             else
                 w4 = fp4x8_scaled(v, exp2i(max(e4, kMinScaledExp)));
-            store_stream(c4 + 16 * (DA2_DPAD / 2) * it + o4, w4);
+            *reinterpret_cast<uint32_t*>(c4 + 16 * (DA2_DPAD / 2) * it + o4) = w4;
             if ((cc & 3) == 0) s4[16 * (DA2_DPAD / 32) * it + os4] = (uint8_t)(e4 + 127);
             float x[8];
             unpack8(v, x);
