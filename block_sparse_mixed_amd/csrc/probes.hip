@@ -110,6 +110,18 @@ __global__ void k_mfma_fp8_k16(const uint8_t* a, const uint8_t* b, float* d) {
     for (int j = 0; j < 16; ++j) d[(8 * (j >> 2) + 4 * h + (j & 3)) * 32 + r] = acc[j];
 }
 
+// One V_MFMA_F64_16X16X4_F64 with the lane layout the draft logits kernel
+// assumes: lane l gives A[l % 16][l / 16] and B[l / 16][l % 16]; its result
+// element e is written to d[(l / 16 + 4 e) * 16 + l % 16]. a is A [16][4],
+// b is B [4][16], both row-major; d receives A B [16][16] if the assumption
+// holds.
+__global__ void k_mfma_f64(const double* a, const double* b, double* d) {
+    const int l = threadIdx.x;
+    const int r = l & 15, g = l >> 4;
+    const v4d acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[r * 4 + g], b[g * 16 + r], (v4d){0.0, 0.0, 0.0, 0.0}, 0, 0, 0);
+    for (int e = 0; e < 4; ++e) d[(g + 4 * e) * 16 + r] = acc[e];
+}
+
 // out[i] = E4M3 code (fmt 0) or E2M1 code (fmt 1, one per byte) of the bf16
 // value in[i] converted with v_cvt_scalef32_pk_fp8_bf16 / _fp4_bf16 and the
 // given scale operand; n even.
@@ -389,6 +401,12 @@ int da2p_mfma_fp8(const uint8_t* a, const uint8_t* b, float* d, int path) {
         hipLaunchKernelGGL(k_mfma_fp8, dim3(1), dim3(64), 0, 0, a, b, d);
     else
         return -1;
+    return (int)hipDeviceSynchronize();
+}
+
+// a: device double[16 * 4]; b: device double[4 * 16]; d: device double[16 * 16]
+int da2p_mfma_f64(const double* a, const double* b, double* d) {
+    hipLaunchKernelGGL(k_mfma_f64, dim3(1), dim3(64), 0, 0, a, b, d);
     return (int)hipDeviceSynchronize();
 }
 

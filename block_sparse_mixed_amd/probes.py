@@ -35,6 +35,7 @@ def lib():
         _lib.da2p_to_fp8.argtypes = [P, P, ctypes.c_int]
         _lib.da2p_to_fp4.argtypes = [P, P, ctypes.c_int]
         _lib.da2p_mfma_fp8.argtypes = [P, P, P, ctypes.c_int]
+        _lib.da2p_mfma_f64.argtypes = [P, P, P]
         _lib.da2p_bf16_to.argtypes = [P, ctypes.c_float, P, ctypes.c_int, ctypes.c_int]
         _lib.da2p_issue.argtypes = [ctypes.c_int, ctypes.c_int, P, P]
         _lib.da2p_mem_issue.argtypes = [ctypes.c_int, P, P, P]
@@ -100,6 +101,18 @@ def mfma_fp8(a_codes: np.ndarray, b_codes: np.ndarray, path: str) -> np.ndarray:
     d = torch.empty(32 * 32, dtype=torch.float32, device="cuda")
     _ok(lib().da2p_mfma_fp8(a.data_ptr(), b.data_ptr(), d.data_ptr(), MFMA_PATHS[path]), "mfma_fp8")
     return d.cpu().numpy().reshape(32, 32)
+
+
+def mfma_f64(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """One 16x16x4 fp64 MFMA on A [16][4] and B [4][16], read back with the
+    result layout the draft logits kernel assumes (lane l, element e -> row
+    l / 16 + 4 e, column l % 16): equals A @ B when that layout holds."""
+    import torch
+    at = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).cuda()
+    bt = torch.from_numpy(np.ascontiguousarray(b, dtype=np.float64)).cuda()
+    d = torch.empty(16 * 16, dtype=torch.float64, device="cuda")
+    _ok(lib().da2p_mfma_f64(at.data_ptr(), bt.data_ptr(), d.data_ptr()), "mfma_f64")
+    return d.cpu().numpy().reshape(16, 16)
 
 
 # flops per MFMA instruction of kinds 5, 6, 7, 8

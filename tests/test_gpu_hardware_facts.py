@@ -141,3 +141,17 @@ def test_bf16_mfma_is_exact_and_the_f8f6f4_mfma_is_not(probes):
     assert worst16 <= 64 * 2.0 ** -24
     assert worst8 > 64 * 2.0 ** -24
     assert worst8k16 > 64 * 2.0 ** -24
+
+
+@pytest.mark.gpu
+def test_f64_mfma_result_rows_are_lane_group_plus_four_element(probes):
+    # The layout the draft logits kernel builds on: lane l feeds A[l % 16][l / 16]
+    # and B[l / 16][l % 16], and its result element e is D[l / 16 + 4 e][l % 16].
+    # With distinct small integers the product is exact, so any other row map
+    # shows as a mismatch.
+    rng = np.random.default_rng(3)
+    a = rng.integers(-8, 9, size=(16, 4)).astype(np.float64)
+    b = rng.integers(-8, 9, size=(4, 16)).astype(np.float64)
+    a[:, 0] += 100.0 * np.arange(16)        # every row of A @ B distinct
+    d = probes.mfma_f64(a, b)
+    assert np.array_equal(d, a @ b)
