@@ -212,17 +212,6 @@ __device__ __forceinline__ int compact_list(const int8_t* lab, int nb, int8_t wa
 __device__ __forceinline__ bool before(double va, int ia, double vb, int ib) {
     return (va > vb) | ((va == vb) & (ia < ib));
 }
-// The same order on the value alone (kKeyOnly): the bits of a non-negative
-// double compared as signed 64-bit integers, in which the padding value -1.0
-// comes below every real C >= 0. One comparison instead of three; it leaves
-// equal values in any order, which the caller checks for.
-template <bool kKeyOnly>
-__device__ __forceinline__ bool ordered_before(double va, int ia, double vb, int ib) {
-    if constexpr (kKeyOnly)
-        return __builtin_bit_cast(int64_t, va) > __builtin_bit_cast(int64_t, vb);
-    else
-        return before(va, ia, vb, ib);
-}
 
 // Bitonic sort of np = 256 R (value, index) pairs held in registers: lane l
 // of wave w holds elements 64 R w + R l .. + R - 1. A compare-exchange step
@@ -242,14 +231,14 @@ struct SortState {
 // In-lane compare-exchange at a compile-time distance J < R, so that every
 // register index is a constant (a run-time distance would index the arrays
 // dynamically and move them to scratch memory).
-template <int R, int J, bool kKeyOnly>
+template <int R, int J>
 __device__ __forceinline__ void inlane_step(SortState<R>& st, int base, int k) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         if (r & J) continue;
         const int r2 = r | J;
         const bool fwd = ((base + r) & k) == 0;
-        const bool swap = fwd != ordered_before<kKeyOnly>(st.v[r], st.ix[r], st.v[r2], st.ix[r2]);
+        const bool swap = fwd != before(st.v[r], st.ix[r], st.v[r2], st.ix[r2]);
         const double a = st.v[r], b = st.v[r2];
         const int ia = st.ix[r], ib = st.ix[r2];
         st.v[r] = swap ? b : a;
@@ -260,21 +249,21 @@ __device__ __forceinline__ void inlane_step(SortState<R>& st, int base, int k) {
 }
 
 // run-time distance jj < R -> the matching compile-time step
-template <int R, bool kKeyOnly, int J = 1>
+template <int R, int J = 1>
 __device__ __forceinline__ void inlane_dispatch(SortState<R>& st, int base, int k, int jj) {
     if constexpr (J < R) {
         if (jj == J) {
-            inlane_step<R, J, kKeyOnly>(st, base, k);
+            inlane_step<R, J>(st, base, k);
             return;
         }
-        inlane_dispatch<R, kKeyOnly, 2 * J>(st, base, k, jj);
+        inlane_dispatch<R, 2 * J>(st, base, k, jj);
     }
 }
 
-template <int R, int D = 0, bool kKeyOnly = false>
+template <int R, int D = 0>
 __device__ __forceinline__ void bitonic_step(SortState<R>& st, double* val, int32_t* idx, int base, int k, int jj) {
     if (jj < R) {
-        inlane_dispatch<R, kKeyOnly>(st, base, k, jj);
+        inlane_dispatch<R>(st, base, k, jj);
         return;
     }
     double pv[R];
@@ -309,7 +298,7 @@ __device__ __forceinline__ void bitonic_step(SortState<R>& st, double* val, int3
     for (int r = 0; r < R; ++r) {
         const int e = base + r;
         const bool want_first = ((e & jj) == 0) == ((e & k) == 0);
-        const bool take = ordered_before<kKeyOnly>(st.v[r], st.ix[r], pv[r], pi[r]) != want_first;
+        const bool take = before(st.v[r], st.ix[r], pv[r], pi[r]) != want_first;
         st.v[r] = take ? pv[r] : st.v[r];
         st.ix[r] = take ? pi[r] : st.ix[r];
     }
@@ -317,14 +306,14 @@ __device__ __forceinline__ void bitonic_step(SortState<R>& st, double* val, int3
 
 // compile-time stages for the small sizes (every condition of a step folds
 // away); a plain loop for the large ones, whose full unrolling is too big
-template <int R, int K, int JJ, int NP = 256 * R, bool kKeyOnly = false>
+template <int R, int K, int JJ, int NP = 256 * R>
 __device__ __forceinline__ void bitonic_stages(SortState<R>& st, double* val, int32_t* idx, int base) {
     if constexpr (K <= NP) {
-        bitonic_step<R, (JJ >= R && JJ < 64 * R) ? JJ / R : 0, kKeyOnly>(st, val, idx, base, K, JJ);
+        bitonic_step<R, (JJ >= R && JJ < 64 * R) ? JJ / R : 0>(st, val, idx, base, K, JJ);
         if constexpr (JJ > 1)
-            bitonic_stages<R, K, JJ / 2, NP, kKeyOnly>(st, val, idx, base);
+            bitonic_stages<R, K, JJ / 2, NP>(st, val, idx, base);
         else
-            bitonic_stages<R, 2 * K, K, NP, kKeyOnly>(st, val, idx, base);
+            bitonic_stages<R, 2 * K, K, NP>(st, val, idx, base);
     }
 }
 
@@ -485,18 +474,8 @@ __global__ __launch_bounds__(256) void rank_wave_kernel(Geo g, double* __restric
     }
 
     // bitonic sort, "a before b" iff C_a > C_b or (C_a == C_b and index_a < index_b);
-    // every step's partner is in the lane or in the wave. It runs on C alone
-    // (one comparison a step); equal real values end up adjacent, and only if
-    // a row has such a pair does the index decide, in a second, exact sort.
-    bitonic_stages<R, 2, 1, np, true>(st, nullptr, nullptr, base);
-    {
-        bool tie = false;
-#pragma unroll
-        for (int r = 0; r + 1 < R; ++r) tie |= (st.v[r] == st.v[r + 1]) & (st.v[r] >= 0.0);
-        const double next = __shfl_down(st.v[0], 1);     // the next lane's first element
-        tie |= (lane < 63) & (st.v[R - 1] == next) & (next >= 0.0);
-        if (__ballot(tie) != 0ull) bitonic_stages<R, 2, 1, np, false>(st, nullptr, nullptr, base);
-    }
+    // every step's partner is in the lane or in the wave
+    bitonic_stages<R, 2, 1, np>(st, nullptr, nullptr, base);
 
     const int n_ret = g.n_hi + g.n_lo;
     const uint64_t rowid = (uint64_t)bh * nb + i;

@@ -126,6 +126,15 @@ def check_prepare(run: GpuRun, bh: int, st: P.HeadState):
     if diff.any():
         ex = D.exemption_mask(st.scores, n_hi, n_lo)
         assert not (diff & ~ex).any(), "labels differ outside the exemption band"
+    # every row also follows the ranking rule on the GPU's own C (C
+    # descending, lower index first), which decides what the band leaves
+    # open: rows of exactly equal scores, for one
+    order = np.lexsort((np.broadcast_to(np.arange(nb), C.shape), -C), axis=-1)
+    ranked = np.full((nb, nb), D.SKIP, dtype=np.int8)
+    rows = np.arange(nb)[:, None]
+    ranked[rows, order[:, :n_hi]] = D.HI
+    ranked[rows, order[:, n_hi:n_hi + n_lo]] = D.LO
+    assert np.array_equal(lab, ranked), "labels break the (C descending, index ascending) rule on the GPU's C"
     # lists: the labelled blocks in rank order (the GPU's own C descending, lower index first)
     for name, lv, n in (("hi", D.HI, n_hi), ("lo", D.LO, n_lo)):
         if not n:

@@ -233,13 +233,17 @@ def test_zero_and_tiny_magnitude_blocks(da2):
     st = run.oracle_head(0)
     assert st.ops["q8_exp"][0] == -127 and st.ops["q8_exp"][9] + st.ops["k8_exp"][1] < -140
     assert st.labels[0, 1] == D.HI and st.labels[9, 1] != D.SKIP
-    _full_parity(da2, w)
+    assert np.ptp(st.scores[0]) == 0.0                   # the zero query block's scores all tie
+    # these inputs' codes, pools, scores, labels and lists, then attention
+    # with the GPU's own labels, then with the oracle's injected
+    check_prepare(run, 0, st)
     out = run.attend()
     assert torch.isfinite(out).all()
     lab = run.sec("labels", torch.int8, (1, run.nb, run.nb))[0]
     same = np.flatnonzero((lab == st.labels).all(axis=1))
     worst, _ = compare_outputs(np64(out[0, 0]), P.attention_raster(st, blocks=same), block_rows(st, same))
     assert worst <= OUT_TOL
+    _full_parity(da2, w, run=run, states={0: st})
 
 
 @pytest.mark.parametrize("grid", [66, 94])
@@ -252,6 +256,38 @@ def test_prepare_large_block_counts(da2, grid):
     run = GpuRun(da2, w)
     say(f"check prepare {w.name} nb={run.nb}")
     check_prepare(run, 0, run.oracle_head(0))
+
+
+@pytest.mark.parametrize("grid", [40, 60, 66])
+def test_ranking_ties_at_every_sort_size(da2, grid):
+    # 2x2-token windows give 400, 900 and 1089 blocks: the one-wave ranking
+    # with 8 and 16 pairs a lane and the workgroup ranking. Copies of one key
+    # window have equal logits in both maps, so they tie in every row, in
+    # the fp8 list, in the MXFP4 list and across both budget thresholds;
+    # the rows of all-zero query windows are ties throughout. The order of
+    # equal scores, by index, then decides labels and lists.
+    w = dataclasses.replace(S.TINY, name=f"ties{grid}", frames=1, grid_h=grid, grid_w=grid, win_h=2, win_w=2,
+                            head_dim=64, budget_hi=0.1, budget_lo=0.2)
+    q, k, v = S.make_qkv(w)
+    g = lambda t: t.view(w.batch, w.heads, w.grid_h, w.grid_w, w.head_dim)
+    src = g(k)[:, :, 2:4, 4:6].clone()
+    copies = []
+    for y in range(0, grid, 6):
+        x = (3 * y) % grid
+        g(k)[:, :, y:y + 2, x:x + 2] = src                            # copies of key window (1, 2)
+        copies.append((y // 2) * (grid // 2) + x // 2)
+    g(q)[:, :, 0:2, 0:2] = 0                                          # zero query windows
+    g(q)[:, :, grid - 2:grid, 10:12] = 0
+    run = GpuRun(da2, w, qkv=(q, k, v))
+    say(f"check prepare {w.name} nb={run.nb}")
+    st = run.oracle_head(0)
+    nb, n_hi, n_ret = run.nb, st.n_hi, st.n_hi + st.n_lo
+    rank = np.argsort(np.lexsort((np.broadcast_to(np.arange(nb), st.scores.shape), -st.scores), axis=-1), axis=-1)
+    rc = rank[:, copies]
+    assert np.ptp(st.scores[0]) == 0.0 and np.ptp(st.scores[1, copies]) == 0.0
+    for t in (n_hi, n_ret):                                           # ties across each threshold
+        assert ((rc.min(1) < t) & (rc.max(1) >= t)).sum() > 0
+    check_prepare(run, 0, st)
 
 
 def test_attention_long_tile_lists(da2):
