@@ -203,8 +203,17 @@ __device__ __forceinline__ int compact_list(const int8_t* lab, int nb, int8_t wa
         if (hit && p < cap) out[p] = j;
         count += __popcll(mask);
     }
+    // a row with fewer such labels than the list holds: the rest of the list
+    // gets block 0, so that every list entry names a real block
+    for (int p = count + lane; p < cap; p += 64) out[p] = 0;
     return count;
 }
+
+// The value a block's score C sorts by: C itself (C >= 0), or -0.5 for a NaN
+// score (non-finite inputs), so that the order stays total, such blocks rank
+// after every real score and before the padding (-1.0), and the lists remain
+// a permutation of real blocks whatever the inputs held.
+__device__ __forceinline__ double sort_key(double c) { return c >= 0.0 ? c : -0.5; }
 
 // "a before b" in rank order: larger C first, then the lower block index.
 // Bitwise operators, so that the three comparisons combine as lane masks
@@ -391,7 +400,7 @@ __global__ __launch_bounds__(256) void rank_kernel(Geo g, double* __restrict__ s
     for (int j = tid; j < np; j += 256) {
         if (j < nb) {
             const double c = 0.5 * (val[j] / sm + val2[j] / sm2);
-            val[j] = c;
+            val[j] = sort_key(c);
             idx[j] = j;
             row_avg[j] = c;     // section 0 of the scores now holds C for this row
         } else {
@@ -466,8 +475,9 @@ __global__ __launch_bounds__(256) void rank_wave_kernel(Geo g, double* __restric
         const int j = base + r;
         st.ix[r] = j;
         if (j < nb) {
-            st.v[r] = 0.5 * (va[r] / sm + vm[r] / sm2);
-            row_avg[j] = st.v[r];   // section 0 of the scores now holds C for this row
+            const double c = 0.5 * (va[r] / sm + vm[r] / sm2);
+            st.v[r] = sort_key(c);
+            row_avg[j] = c;         // section 0 of the scores now holds C for this row
         } else {
             st.v[r] = -1.0;         // sorts after every real score (C >= 0)
         }

@@ -33,6 +33,12 @@
  *  - Every call that takes a workspace also takes its size in bytes
  *    (workspace_bytes): a buffer smaller than the plan's workspace_bytes, or
  *    not 256-byte aligned, is DA2_ERR_WORKSPACE.
+ *  - q, k and v are expected to hold finite values. Non-finite values give
+ *    unspecified labels and outputs, but the kernels still access only the
+ *    caller's buffers: the ranking sorts a NaN score below every real score,
+ *    so its lists stay a permutation of real blocks, and every list entry
+ *    that da2_prepare or da2_set_labels writes names a real block (the
+ *    attention kernel reads tiles through these lists).
  *  - Argument errors are reported synchronously, before anything is enqueued.
  *    Kernel faults surface at the caller's next synchronisation, as usual in
  *    HIP. No C++ exception crosses this interface.
@@ -208,7 +214,10 @@ da2_status da2_attention(const da2_plan_t* plan, const void* workspace, size_t w
 /* Test hook, not for production: replace the labels in the workspace with
  * labels_dev (device int8 [BH][NB][NB]) and rebuild the hi/lo lists. A row
  * whose label counts differ from (n_hi, n_lo) is counted in status[0] (the
- * count is reset first) and its lists are left unspecified. Asynchronous. */
+ * count is reset first) and its lists are left unspecified (every entry a
+ * real block, block 0 where the row has too few labels): da2_attention then
+ * gives that row unspecified outputs, still reading only the workspace.
+ * Asynchronous. */
 da2_status da2_set_labels(const da2_plan_t* plan, void* workspace, size_t workspace_bytes,
                           const int8_t* labels_dev, void* hip_stream);
 
