@@ -179,18 +179,87 @@ def da2_plan(cfg: Config) -> Plan:
     return Plan(h.value, cfg)
 
 
+def _strides(plan: Plan, out: bool):
+    """Element strides (b, h, n) the kernels use for q/k/v, or for out."""
+    c = plan.cfg
+    s = (c.stride_b, c.stride_h, c.stride_n)
+    if out and (c.out_stride_b or c.out_stride_h or c.out_stride_n):
+        s = (c.out_stride_b, c.out_stride_h, c.out_stride_n)
+    if not any(s):
+        n, d = int(plan.info.tokens), c.head_dim
+        s = (c.heads * n * d, n * d, d)
+    return s
+
+
+def _check_tensor(t, what: str, dtypes, need_elems: int):
+    """A tensor argument (raw integer pointers are passed on unchecked): its
+    dtype, and that its storage holds the need_elems elements the kernels
+    touch from its first element on."""
+    if t is None or isinstance(t, int):
+        return
+    if t.dtype not in dtypes:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected one of {tuple(str(x) for x in dtypes)}")
+    avail = t.untyped_storage().nbytes() - t.storage_offset() * t.element_size()
+    if need_elems * t.element_size() > avail:
+        raise ValueError(f"{what}: the plan reaches {need_elems} elements from its start, its storage holds "
+                         f"{avail // t.element_size()}")
+
+
+def _check_on_gpu(**tensors):
+    for what, t in tensors.items():
+        if t is not None and not isinstance(t, int) and t.device.type != "cuda":
+            raise ValueError(f"{what} must be on a GPU")
+
+
+def _qkv_elems(plan: Plan, out: bool) -> int:
+    c = plan.cfg
+    sb, sh, sn = _strides(plan, out)
+    return (c.batch - 1) * sb + (c.heads - 1) * sh + (int(plan.info.tokens) - 1) * sn + c.head_dim
+
+
+def _check_inputs(plan: Plan, q, k, v):
+    import torch
+    n = _qkv_elems(plan, False)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(t, name, (torch.bfloat16,), n)
+
+
+def _check_out(plan: Plan, out):
+    import torch
+    dt = torch.float32 if plan.cfg.out_dtype == DA2_OUT_FP32 else torch.bfloat16
+    _check_tensor(out, "out", (dt,), _qkv_elems(plan, True))
+
+
+def _check_workspace(workspace):
+    import torch
+    _check_tensor(workspace, "workspace", (torch.uint8, torch.int8), 0)
+
+
+# The enqueue calls check their tensor arguments (dtype, extent, device)
+# before calling the library, which sees only pointers.
 def da2_prepare(plan: Plan, q, k, v, workspace, stream=None):
+    _check_inputs(plan, q, k, v)
+    _check_workspace(workspace)
+    _check_on_gpu(q=q, k=k, v=v, workspace=workspace)
     nbytes = workspace.numel() if hasattr(workspace, "numel") else int(plan.info.workspace_bytes)
     _check(_lib.da2_prepare(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(workspace), nbytes, _stream(stream)),
            "da2_prepare")
 
 
 def da2_attention(plan: Plan, workspace, out, stream=None):
+    _check_workspace(workspace)
+    _check_out(plan, out)
+    _check_on_gpu(workspace=workspace, out=out)
     nbytes = workspace.numel() if hasattr(workspace, "numel") else int(plan.info.workspace_bytes)
     _check(_lib.da2_attention(plan.handle, _ptr(workspace), nbytes, _ptr(out), _stream(stream)), "da2_attention")
 
 
 def da2_set_labels(plan: Plan, workspace, labels, stream=None):
+    import torch
+    nb = int(plan.info.n_blocks)
+    _check_workspace(workspace)
+    _check_tensor(labels, "labels", (torch.int8,), plan.cfg.batch * plan.cfg.heads * nb * nb)
+    _check_on_gpu(workspace=workspace, labels=labels)
     nbytes = workspace.numel() if hasattr(workspace, "numel") else int(plan.info.workspace_bytes)
     _check(_lib.da2_set_labels(plan.handle, _ptr(workspace), nbytes, _ptr(labels), _stream(stream)),
            "da2_set_labels")
@@ -198,6 +267,9 @@ def da2_set_labels(plan: Plan, workspace, labels, stream=None):
 
 def da2_forward_scratch(plan: Plan, q, k, v, out, stream=None):
     """da2_prepare + da2_attention on the library's static workspace (no allocation)."""
+    _check_inputs(plan, q, k, v)
+    _check_out(plan, out)
+    _check_on_gpu(q=q, k=k, v=v, out=out)
     _check(_lib.da2_forward_scratch(plan.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _stream(stream)),
            "da2_forward_scratch")
 

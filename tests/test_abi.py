@@ -178,6 +178,43 @@ def test_wrapper_rejects_mismatched_tensors_before_any_call():
         da2.attention(q, q, q, *args, out_dtype=torch.float16)
 
 
+def test_binding_checks_tensor_arguments_before_any_call():
+    # tensors handed to the binding's enqueue calls: their dtype, an extent
+    # that covers every element the plan's strides reach, and a GPU device,
+    # all checked before the library sees a pointer (these are CPU tensors)
+    import torch
+    n, d = 64, 32
+    p = da2.da2_plan(da2.make_config(1, 2, 1, 8, 8, d, 4, 4, 0.25, 0.25))       # fp32 output
+    full = torch.zeros(1, 2, n, d, dtype=torch.bfloat16)
+    ws = torch.zeros(int(p.info.workspace_bytes), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="storage holds"):
+        da2.da2_prepare(p, torch.zeros(2 * n * d - 1, dtype=torch.bfloat16), full, full, ws)   # one short
+    with pytest.raises(ValueError, match="dtype"):
+        da2.da2_prepare(p, full, full.float(), full, ws)
+    with pytest.raises(ValueError, match="workspace: dtype"):
+        da2.da2_prepare(p, full, full, full, ws.view(torch.int32))
+    with pytest.raises(ValueError, match="q must be on a GPU"):
+        da2.da2_prepare(p, full, full, full, ws)                                # the right sizes, on the CPU
+    with pytest.raises(ValueError, match="out: dtype"):
+        da2.da2_attention(p, ws, full)                                          # the plan writes fp32
+    with pytest.raises(ValueError, match="storage holds"):
+        da2.da2_attention(p, ws, torch.zeros(1, 2, n - 1, d))
+    with pytest.raises(ValueError, match="storage holds"):
+        da2.da2_forward_scratch(p, full, full, full, torch.zeros(1, 2, n, d - 1))
+    with pytest.raises(ValueError, match="labels: dtype"):
+        da2.da2_set_labels(p, ws, torch.zeros(2, 16, 16, dtype=torch.uint8))
+    # slices of a fused [B, N, 3, H, d] buffer: the strides reach past each
+    # slice's own rows, and the last slice ends where the buffer does
+    qkv = torch.zeros(1, n, 3, 2, d, dtype=torch.bfloat16)
+    sp = da2.da2_plan(da2.make_config(1, 2, 1, 8, 8, d, 4, 4, 0.25, 0.25, strides=(n * 6 * d, d, 6 * d)))
+    q, k, v = (qkv[:, :, i].transpose(1, 2) for i in range(3))
+    with pytest.raises(ValueError, match="q must be on a GPU"):
+        da2.da2_prepare(sp, q, k, v, ws)                                        # extents fine
+    cut = torch.zeros(qkv.numel() - 1, dtype=torch.bfloat16)                  # a buffer one element short
+    with pytest.raises(ValueError, match="v: the plan reaches"):
+        da2.da2_prepare(sp, q, k, cut[4 * d:], ws)                              # v's slice of it
+
+
 def test_enqueue_calls_reject_unaligned_pointers_and_strides():
     # q, k, v and out are read and written in 16-byte vectors: their pointers
     # must be 16-byte aligned and the strides multiples of 8 elements, else
