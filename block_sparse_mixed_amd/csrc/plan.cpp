@@ -36,11 +36,13 @@ extern "C" da2_status da2_plan(const da2_config* cfg, da2_plan_t** out) {
     g.grid_w = c.grid_w;
     g.win_h = c.win_h;
     g.win_w = c.win_w;
-    g.n_wy = (c.grid_h + c.win_h - 1) / c.win_h;
-    g.n_wx = (c.grid_w + c.win_w - 1) / c.win_w;
-    g.block_size = c.win_h * c.win_w;
-    int64_t nb = (int64_t)c.frames * g.n_wy * g.n_wx;
+    const int64_t n_wy = ((int64_t)c.grid_h + c.win_h - 1) / c.win_h;
+    const int64_t n_wx = ((int64_t)c.grid_w + c.win_w - 1) / c.win_w;
+    int64_t nb = (int64_t)c.frames * n_wy * n_wx;
     if (nb > DA2_MAX_BLOCKS) return DA2_ERR_UNSUPPORTED;
+    g.n_wy = (int32_t)n_wy;
+    g.n_wx = (int32_t)n_wx;
+    g.block_size = c.win_h * c.win_w;
     g.pack = (c.flags & DA2_FLAG_PACK_EDGES) ? 1 : 0;
     g.fwy = c.grid_h / c.win_h;
     g.fwx = c.grid_w / c.win_w;
@@ -53,6 +55,15 @@ extern "C" da2_status da2_plan(const da2_config* cfg, da2_plan_t** out) {
     g.heads = c.heads;
     int64_t bh = (int64_t)c.batch * c.heads;
     if (bh > 65535) return DA2_ERR_UNSUPPORTED;
+    // Every launch's size along x, in work-items, fits the 32 bits of the
+    // dispatch: the attention kernel runs one 512-thread workgroup per
+    // (b*h, query block), the draft logits one 256-thread workgroup per 32x32
+    // tile of each of the two maps of every b*h.
+    {
+        const uint64_t t = (uint64_t)(nb + 31) / 32;
+        if ((uint64_t)bh * (uint64_t)nb * 512u > UINT32_MAX || 2u * (uint64_t)bh * t * t * 256u > UINT32_MAX)
+            return DA2_ERR_UNSUPPORTED;
+    }
     g.bh = (int32_t)bh;
     g.tokens = (int64_t)c.frames * c.grid_h * c.grid_w;
 

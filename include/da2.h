@@ -162,7 +162,11 @@ typedef struct da2_plan_info_s {
  * when any stride is given; the same for the out_stride_* triple), budgets outside [0, 1] or not finite, a
  * negative or non-finite softmax_scale, an unknown out_dtype or flag bit,
  * or n_ret = 0; DA2_ERR_UNSUPPORTED for a head_dim or window outside the
- * domains above, more than DA2_MAX_BLOCKS blocks, or batch * heads > 65535.
+ * domains above, more than DA2_MAX_BLOCKS blocks, batch * heads > 65535, or
+ * a launch whose work-items along x exceed 32 bits: batch * heads * NB >
+ * 8388607 (attention, 512 work-items per (b*h, query block)) or
+ * batch * heads * ceil(NB / 32)^2 > 8388607 (draft logits, 2 x 256 per
+ * 32 x 32 tile).
  * Geometry [DraftAttention (arXiv 2505.14708), abstract; news article on it,
  * method steps 1 and 4]: each frame is cut into win_h x win_w windows, padded
  * up to whole windows; a window is one block (with DA2_FLAG_PACK_EDGES: the

@@ -95,11 +95,25 @@ def test_budget_counts_agree_with_oracle_on_many_configs():
     (dict(flags=2), da2.DA2_ERR_INVALID_ARG),
     (dict(flags=3), da2.DA2_ERR_INVALID_ARG),
     (dict(frames=200, grid_h=64, grid_w=64), da2.DA2_ERR_UNSUPPORTED),
+    (dict(grid_h=2 ** 31 - 1), da2.DA2_ERR_UNSUPPORTED),
+    # launches past 32 bits of work-items: the attention grid (32000 x 336
+    # workgroups of 512), the draft logits grid (600 x 2 x 128^2 of 256)
+    (dict(batch=2000, heads=16), da2.DA2_ERR_UNSUPPORTED),
+    (dict(batch=600, heads=1, frames=128, grid_h=64, grid_w=64), da2.DA2_ERR_UNSUPPORTED),
 ])
 def test_plan_rejects(kw, status):
     with pytest.raises(da2.Da2Error) as e:
         da2.da2_plan(_cfg(**kw))
     assert e.value.status == status
+
+
+def test_plan_accepts_the_largest_launches():
+    # just inside both launch limits: 511 x 2 x 128^2 draft-logits workgroups
+    # of 256 and 511 x 4096 attention workgroups of 512 work-items
+    p = da2.da2_plan(_cfg(batch=511, heads=1, frames=128, grid_h=64, grid_w=64))
+    assert p.info.n_blocks == 4096
+    p = da2.da2_plan(_cfg(batch=1560, heads=16, frames=21))        # 24960 x 336 attention workgroups
+    assert 24960 * 336 * 512 <= 2 ** 32 - 1
 
 
 def test_plan_clamps_lo_budget():
