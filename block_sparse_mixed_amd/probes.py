@@ -40,6 +40,7 @@ def lib():
         _lib.da2p_issue.argtypes = [ctypes.c_int, ctypes.c_int, P, P]
         _lib.da2p_mem_issue.argtypes = [ctypes.c_int, P, P, P]
         _lib.da2p_lds_read.argtypes = [ctypes.c_int, P, P]
+        _lib.da2p_stream.argtypes = [P, P, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, P]
     return _lib
 
 
@@ -196,6 +197,30 @@ def lds_read_rate(waves: int):
     return c / reads, waves * reads * 1024 / c, 256 * waves * reads * 1024 / wall / 1e12
 
 
+# The preparation's algorithmic traffic at the Wan-480p shape (12 heads,
+# 32760 tokens, d 128): the bf16 Q, K and V read once (exact), and about
+# 312 MB of codes, scales and pools for the padded tiles written.
+PREP_READ_BYTES = 3 * 12 * 32760 * 128 * 2
+PREP_WRITE_BYTES = 312_000_000
+
+
+def stream_bandwidth(read_bytes: int, write_bytes: int, grids=(1024, 2048, 4096, 8192), reps: int = 5):
+    """{grid: TB/s} of a plain streaming kernel that reads read_bytes and
+    writes write_bytes: the shortest of `reps` launches after a warm-up, each
+    timed alone with HIP events in the probe library."""
+    import torch
+    read_bytes, write_bytes = read_bytes // 16 * 16, write_bytes // 16 * 16
+    src = torch.ones(max(read_bytes, 16), dtype=torch.uint8, device="cuda")
+    dst = torch.empty(max(write_bytes, 16), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    out = {}
+    for grid in grids:
+        ms = ctypes.c_float()
+        _ok(lib().da2p_stream(src.data_ptr(), dst.data_ptr(), read_bytes, write_bytes, grid, reps, ctypes.byref(ms)),
+            "stream")
+        out[grid] = (read_bytes + write_bytes) / (ms.value * 1e-3) / 1e12
+    return out
+
 def main():
     import torch
     print(f"device: {torch.cuda.get_device_name(0)}")
@@ -233,6 +258,13 @@ def main():
     for waves in (4, 8, 16):
         per, bpc, tbs = lds_read_rate(waves)
         print(f"| {waves} | {per:.1f} | {bpc:.0f} | {tbs:.0f} |")
+    print("\nstreaming HBM bandwidth of a plain kernel (16-byte accesses, 256 threads a workgroup), best of 5:")
+    print("\n| traffic | 1024 groups | 2048 | 4096 | 8192 |")
+    print("|---|---|---|---|---|")
+    for name, r, w in (("the preparation's volume at Wan-480p: 302 MB read + 312 MB written", PREP_READ_BYTES,
+                        PREP_WRITE_BYTES), ("302 MB read", PREP_READ_BYTES, 0), ("312 MB written", 0, PREP_WRITE_BYTES)):
+        bw = stream_bandwidth(r, w)
+        print(f"| {name} | " + " | ".join(f"{bw[g]:.2f} TB/s" for g in (1024, 2048, 4096, 8192)) + " |")
 
 if __name__ == "__main__":
     main()
