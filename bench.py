@@ -148,6 +148,21 @@ def flops(w, nb, n_hi, n_lo):
     return dense, f_hi, f_lo
 
 
+def real_slot_flops(w, info, labels):
+    """MFMA work on real key and query slots only, (F_hi, F_lo): per retained
+    (query block, key block) pair 4 d n_q n_k flops with the blocks' real
+    token counts, where the executed figures count all 128 x 128 slots."""
+    import torch
+
+    import block_sparse_mixed_amd as da2
+    cnt = torch.bincount(token_blocks(w, info, "cpu"), minlength=info.n_blocks).double()
+    out = []
+    for lab in (da2.DA2_HI, da2.DA2_LO):
+        m = (labels == lab).double()
+        out.append(4.0 * w.head_dim * float(torch.einsum("i,bij,j->", cnt, m, cnt)))
+    return tuple(out)
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
@@ -474,7 +489,9 @@ def time_layout(w, qd, kd, vd, pack, steps, warmup):
     prep_ms = [e[0].elapsed_time(e[1]) for e in events]
     attn_ms = [e[1].elapsed_time(e[2]) for e in events]
     step_ms = [e[0].elapsed_time(e[2]) for e in events]
-    return plan.info, prep_ms, attn_ms, step_ms, wall, out
+    nb = plan.info.n_blocks
+    labels = da2.workspace_section(plan, ws, "labels", torch.int8, (w.batch * w.heads, nb, nb)).cpu()
+    return plan.info, prep_ms, attn_ms, step_ms, wall, out, labels
 
 
 def all_configs(args):
@@ -489,7 +506,7 @@ def all_configs(args):
         w = S.WORKLOADS[name]
         qc, kc, vc = S.make_qkv(w)
         q, k, v = (t.to("cuda:0") for t in (qc, kc, vc))
-        info, prep_ms, attn_ms, step_ms, wall, out = time_layout(w, q, k, v, False, args.steps, args.warmup)
+        info, prep_ms, attn_ms, step_ms, wall, out, _ = time_layout(w, q, k, v, False, args.steps, args.warmup)
         dense, f_hi, f_lo = flops(w, info.n_blocks, info.n_hi, info.n_lo)
         t_star = f_hi / P_FP8 + f_lo / P_FP4
         att_s = sum(attn_ms) / len(attn_ms) / 1e3
@@ -615,13 +632,14 @@ def main():
         cpu = cpu_baseline(w, q, k, v, min(args.cpu_heads, w.batch * w.heads), workers)
     dev = torch.device("cuda:0")
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
-    info, prep_ms, attn_ms, step_ms, wall, out = time_layout(w, qd, kd, vd, args.pack_edges, args.steps, args.warmup)
+    info, prep_ms, attn_ms, step_ms, wall, out, labels = time_layout(w, qd, kd, vd, args.pack_edges, args.steps,
+                                                                     args.warmup)
     err = dense_error(qd, kd, vd, out, info.tau, args.error_rows)
     del out
     alt = None
     if not args.no_alt_layout:
-        a_info, a_prep, a_attn, a_step, _, a_out = time_layout(w, qd, kd, vd, not args.pack_edges, args.steps,
-                                                               args.warmup)
+        a_info, a_prep, a_attn, a_step, _, a_out, _ = time_layout(w, qd, kd, vd, not args.pack_edges, args.steps,
+                                                                  args.warmup)
         a_err = dense_error(qd, kd, vd, a_out, a_info.tau, args.error_rows)
         del a_out
         a_dense, a_hi, a_lo = flops(w, a_info.n_blocks, a_info.n_hi, a_info.n_lo)
@@ -642,6 +660,7 @@ def main():
     achieved = (f_hi + f_lo) / attn_avg_s
     # the instructions actually issued: half of F_hi (QK^T) on bf16 MFMAs
     t_star_instr = 0.5 * f_hi / P_BF16 + 0.5 * f_hi / P_FP8 + f_lo / P_FP4
+    r_hi, r_lo = real_slot_flops(w, info, labels)
     res = {
         "metric": METRIC,
         "value": dense / (ms_per_step / 1e3) / 1e12,
@@ -673,6 +692,8 @@ def main():
         "blended_roofline_ms": t_star * 1e3,
         "issued_mix_roofline_ms": t_star_instr * 1e3,
         "flops": {"dense_equiv": dense, "f_hi": f_hi, "f_lo": f_lo},
+        "real_slots": {"f_hi": r_hi, "f_lo": r_lo, "useful_fraction": (r_hi + r_lo) / (f_hi + f_lo),
+                       "attention_tflops": (r_hi + r_lo) / attn_avg_s / 1e12},
         "other_layout": alt,
     }
     print(json.dumps(res), flush=True)
