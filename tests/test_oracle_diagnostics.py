@@ -188,3 +188,32 @@ def test_bench_fidelity_measure_matches_the_oracle(pack, blocks):
     mm = sum(float((M ** 2).sum()) for M in Ms)
     assert got["draft_map_rel_fro"] == pytest.approx((cm / mm) ** 0.5, rel=1e-4)
     assert got["blocks_per_head"] == len(blocks) and got["rows_per_head"] == len(rows[0])
+
+
+@pytest.mark.parametrize("pack", [False, True])
+def test_bench_real_slot_flops_count_real_token_pairs(pack):
+    # the benchmark's useful-work figure: for every retained (query block,
+    # key block) pair, 4 d flops per pair of real tokens, counted here token
+    # by token from the oracle geometry's raster indices (ragged windows)
+    import torch
+
+    import bench
+    import block_sparse_mixed_amd as da2
+
+    cfg = _cfg(frames=2, gh=10, gw=9, d=32, wh=2, ww=4)
+    g = Geometry(cfg.frames, cfg.grid_h, cfg.grid_w, cfg.win_h, cfg.win_w, pack_edges=pack)
+    w = SimpleNamespace(batch=1, heads=2, head_dim=cfg.head_dim, tokens=g.tokens, frames=cfg.frames,
+                        grid_h=cfg.grid_h, grid_w=cfg.grid_w, win_h=cfg.win_h, win_w=cfg.win_w)
+    info = SimpleNamespace(n_blocks=g.n_blocks, n_wy=g.n_wy, n_wx=g.n_wx, n_full=g.n_full, flags=int(pack))
+    rng = np.random.default_rng(7)
+    labels = rng.choice([da2.DA2_SKIP, da2.DA2_LO, da2.DA2_HI], size=(2, g.n_blocks, g.n_blocks))
+    idx = g.raster_index()
+    real = [int((idx[b] >= 0).sum()) for b in range(g.n_blocks)]
+    want = {da2.DA2_HI: 0, da2.DA2_LO: 0}
+    for h in range(2):
+        for i in range(g.n_blocks):
+            for j in range(g.n_blocks):
+                if labels[h, i, j] in want:
+                    want[labels[h, i, j]] += 4 * cfg.head_dim * real[i] * real[j]
+    got = bench.real_slot_flops(w, info, torch.from_numpy(labels.astype(np.int8)))
+    assert got == (want[da2.DA2_HI], want[da2.DA2_LO])
